@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the k-means assignment step on one MI355X.
+
+One step = the whole hot path on one seeded input set: the centroid-norm
+pre-pass (``kmeans_centroid_norms``) followed by ``kmeans_assign``, with the
+three seeded sets (17, 29, 43) resident in HBM and rotated between steps
+(flashlib PR #22, nightly-comparison section, "Benchmark methodology":
+rotating seeded bf16 sets, warmup calls, then timed calls).
+
+Prints one JSON line.  ``value`` = points assigned per second over the timed
+steps (GPU-event time, inputs already on the device).  ``roofline`` reports
+the assign kernel against the bf16 dense MFMA peak, with its average launch
+duration measured by HIP events on the launch stream.  ``cpu_baseline`` times
+the CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from means_nearest_centroid_amd import workloads as W  # noqa: E402
+
+METRIC = "points assigned/sec + % bf16 MFMA peak at N=262144,D=128,K=4096 (1 GPU)"
+BF16_DENSE_PEAK_TFLOPS = 2516.6     # MI355X: 256 CU x 4096 flop/clk x 2.4 GHz
+KERNEL_SOURCES = ("means_nearest_centroid_amd/csrc/kmeans_kernels.hip",
+                  "means_nearest_centroid_amd/csrc/kmeans_internal.h",
+                  "means_nearest_centroid_amd/csrc/kmeans_api.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(config: int):
+    """HBM bytes per assign launch from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_assign_workload{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
+def cpu_baseline(X, C, target_s: float):
+    """Time the oracle on the first points of the workload, growing the
+    sample until one run takes about ``target_s`` seconds."""
+    import oracle
+    n = 64
+    while True:
+        t0 = time.perf_counter()
+        oracle.assign(X[:n], C)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= X.shape[0]:
+            break
+        grow = max(2.0, min(16.0, 1.2 * target_s / max(dt, 1e-3)))
+        n = min(X.shape[0], int(n * grow))
+    return dict(value=n / dt, unit="points/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {n} points of seed {W.SEEDS[0]}, all {C.shape[0]} "
+                       f"centroids, fp64, {dt:.2f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(W.CONFIGS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle sample (0 disables)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter scale)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import means_nearest_centroid_amd as km
+
+    cfg = W.CONFIGS[args.config]
+    N, D, K = cfg["N"], cfg["D"], cfg["K"]
+    print(f"[bench] generating workload {args.config} ({cfg['name']})", file=sys.stderr,
+          flush=True)
+    host_sets = [W.make_config(args.config, s)[:2] for s in W.SEEDS]
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    km.load_library()
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sets = [(to_dev(X), to_dev(C)) for X, C in host_sets]
+    norms = [torch.empty(K, dtype=torch.float32, device=dev) for _ in sets]
+    labels = torch.empty(N, dtype=torch.int32, device=dev)
+    min_dist = torch.empty(N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    plan = km.kmeans_plan(N, D, K)
+
+    def step(i, ev=None):
+        X, C = sets[i % len(sets)]
+        n = norms[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        km.kmeans_centroid_norms(C, n, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        km.kmeans_assign(X, C, n, labels, min_dist, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps bracketed by synchronisation, GPU events on the
+    # launch stream around the whole region and around each kernel.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    norms_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    assign_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    print(f"[bench] {args.steps} steps: {total_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall",
+          file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {nbytes} bytes read, {nbytes} bytes written",
+              file=sys.stderr, flush=True)
+
+    flops = 2.0 * N * D * K
+    avg_assign_s = float(assign_ms.mean()) / 1e3
+    achieved = flops / avg_assign_s / 1e12
+    traffic = traffic_record(args.config)
+    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_DENSE_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / BF16_DENSE_PEAK_TFLOPS, 4),
+                    traffic=(traffic["hbm_bytes_per_launch"] if traffic else None),
+                    kernel="kmeans_assign (assign_kernel"
+                           + (" + merge_kernel" if plan["path"] == km.PATH_SPLIT else "") + ")",
+                    avg_launch_us=round(avg_assign_s * 1e6, 2),
+                    flop_per_launch=flops)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        X0, C0 = host_sets[0]
+        cpu = cpu_baseline(X0, C0, args.cpu_seconds)
+
+    value = N / (ms_per_step / 1e3)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"kmeans assignment, {cfg['name']}, bf16 Gaussian mixture, "
+                        f"seeds {list(W.SEEDS)} rotated",
+            "N": N, "D": D, "K": K, "path": "split" if plan["path"] == 2 else "direct",
+            "splits": plan["splits"],
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown_us": {
+            "norms_median": round(float(np.median(norms_ms)) * 1e3, 2),
+            "assign_median": round(float(np.median(assign_ms)) * 1e3, 2),
+            "assign_min": round(float(assign_ms.min()) * 1e3, 2),
+            "assign_p90": round(float(np.percentile(assign_ms, 90)) * 1e3, 2),
+            "step_mean": round(ms_per_step * 1e3, 2),
+        },
+        "assign_only_points_per_s": N / (float(np.median(assign_ms)) / 1e3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

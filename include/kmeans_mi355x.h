@@ -1,0 +1,143 @@
+/*
+ * kmeans_mi355x.h -- C ABI of the MI355X (gfx950) k-means assignment library.
+ *
+ * The operation.  flashlib PR #22, "Optimize Blackwell k-means assignment
+ * reduction", Summary: the assignment step scores every (point, centroid)
+ * pair from the point-centroid product and the centroid norms and keeps the
+ * best-scoring centroid per point, the smaller index winning a tie; the
+ * "Key ideas and contributions" table (rows "Two-chain argmin" and
+ * "Deterministic winner merge") describes the winner search as independent
+ * chains merged by (score, index).  The score used here is the squared-
+ * Euclidean one,
+ *
+ *     s_ik = ||c_k||^2 - 2 x_i . c_k ,   label_i = lowest k minimising s_ik,
+ *     min_dist_i = ||x_i - c_label_i||^2   (computed as ||x_i||^2 + s_best).
+ *
+ * Non-finite inputs: scores follow IEEE arithmetic and are ranked
+ * -inf < finite < +inf < NaN with ties to the lower index, so a NaN score
+ * wins only when every score is NaN (label 0).  min_dist is NaN or +inf when
+ * x_i or the winning row holds a non-finite value.  Finite inputs must stay
+ * below 2^56 in magnitude (no fp32 overflow for D <= 512).
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller; the
+ *     library keeps no reference after the call returns.
+ *   - Calls are asynchronous on `stream` (NULL = the legacy default stream)
+ *     and never synchronise.  Execution errors surface at the caller's next
+ *     synchronisation on that stream.
+ *   - Arguments are validated on the host before any HIP call.  On a non-OK
+ *     status nothing was launched (except KMEANS_ERR_HIP, where a launch may
+ *     have been attempted) and the outputs are unspecified.
+ *   - kmeans_last_error() returns a thread-local message for the last
+ *     non-OK status on the calling thread.
+ *   - Results are bitwise deterministic for identical inputs and shape; no
+ *     reduction uses atomics.
+ *   - Outputs must not overlap inputs (not checked).
+ */
+#ifndef KMEANS_MI355X_H
+#define KMEANS_MI355X_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KMEANS_ABI_VERSION 1
+
+/* Supported feature dimension: 16 <= D <= 512 and D % 16 == 0. */
+#define KMEANS_MIN_D 16
+#define KMEANS_MAX_D 512
+
+typedef enum {
+    KMEANS_OK = 0,
+    KMEANS_ERR_INVALID_ARG = 1,  /* null pointer, negative size, K < 1 ... */
+    KMEANS_ERR_UNSUPPORTED = 2,  /* D outside the supported set; N or K >= 2^31 */
+    KMEANS_ERR_ALIGNMENT = 3,    /* X/C not 16-byte or outputs not 4-byte aligned */
+    KMEANS_ERR_HIP = 4,          /* a HIP runtime call or launch failed */
+    KMEANS_ERR_NO_MEMORY = 5     /* stream-ordered workspace allocation failed */
+} kmeans_status_t;
+
+typedef enum {
+    KMEANS_PATH_AUTO = 0,    /* shape-based choice (what kmeans_assign does) */
+    KMEANS_PATH_DIRECT = 1,  /* one pass: every workgroup scans all K centroids */
+    KMEANS_PATH_SPLIT = 2    /* K split over `splits` ranges + a merge pass */
+} kmeans_path_t;
+
+/*
+ * Centroid norms, n_k = sum_j c_kj^2 (the "centroid norms" the Summary says
+ * the score tile is combined with), one fp32 value per centroid row.
+ *
+ *   C      bf16 [K][D], row-major, D contiguous, 16-byte aligned.
+ *   K      number of centroid rows, 0 <= K < 2^31 (K == 0: no-op, KMEANS_OK).
+ *   D      feature dimension (see KMEANS_MIN_D / KMEANS_MAX_D).
+ *   norms  fp32 [K], 4-byte aligned, written.
+ *
+ * Squares of bf16 values are exact in fp32; the sum is fp32 with a fixed
+ * order, so bitwise-identical rows get bitwise-identical norms (which the
+ * lowest-index rule of kmeans_assign relies on for duplicate rows).
+ */
+kmeans_status_t kmeans_centroid_norms(const void *C, int64_t K, int64_t D,
+                                      float *norms, hipStream_t stream);
+
+/*
+ * Nearest-centroid assignment (Summary; "Key ideas and contributions").
+ *
+ *   X         bf16 [N][D] points, row-major, 16-byte aligned.
+ *   C         bf16 [K][D] centroids, row-major, 16-byte aligned.
+ *   norms     fp32 [K], ||c_k||^2 as written by kmeans_centroid_norms for
+ *             this C (other values give the scores n_k - 2 x.c_k as passed).
+ *   N         number of points, 0 <= N < 2^31 (N == 0: no-op, KMEANS_OK).
+ *   D         feature dimension, 16 <= D <= 512, D % 16 == 0.
+ *   K         number of centroids, 1 <= K < 2^31.
+ *   labels    int32 [N], written: lowest index minimising s_ik.
+ *   min_dist  fp32 [N], written: squared distance to the chosen centroid,
+ *             max(0, ||x||^2 + s_best) for finite data.
+ *
+ * Small-N / large-K shapes run a K-split path whose stream-ordered scratch
+ * (8 bytes per point per split + 4 bytes per point) comes from
+ * hipMallocAsync/hipFreeAsync on `stream`; KMEANS_ERR_NO_MEMORY if it fails.
+ * Both paths give bitwise-identical outputs.
+ */
+kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms,
+                              int64_t N, int64_t D, int64_t K, int32_t *labels,
+                              float *min_dist, hipStream_t stream);
+
+/*
+ * kmeans_assign with the dispatch forced: `path` as in kmeans_path_t and, for
+ * KMEANS_PATH_SPLIT, `splits` K-ranges (0 = automatic count; clamped to the
+ * number of centroid blocks).  Same arguments, outputs and errors as
+ * kmeans_assign; exists so that the two paths can be compared bit for bit.
+ */
+kmeans_status_t kmeans_assign_path(const void *X, const void *C, const float *norms,
+                                   int64_t N, int64_t D, int64_t K, int32_t *labels,
+                                   float *min_dist, int32_t path, int32_t splits,
+                                   hipStream_t stream);
+
+/*
+ * The launch plan kmeans_assign would use for a shape (host only; makes no
+ * HIP call).  Any output pointer may be NULL.
+ *   path          KMEANS_PATH_DIRECT or KMEANS_PATH_SPLIT
+ *   splits        number of K-ranges (1 on the direct path)
+ *   workgroups    point-workgroups per K-range
+ *   points_per_wg points owned by one workgroup
+ *   k_block       centroid rows staged in LDS per block
+ *   padded_d      D rounded up to the kernel's k-step multiple
+ */
+kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t *path,
+                            int32_t *splits, int32_t *workgroups,
+                            int32_t *points_per_wg, int32_t *k_block,
+                            int32_t *padded_d);
+
+/* Thread-local message for the last non-OK status ("" if none). */
+const char *kmeans_last_error(void);
+
+/* KMEANS_ABI_VERSION of the built library. */
+int kmeans_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KMEANS_MI355X_H */

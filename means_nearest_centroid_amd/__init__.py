@@ -1,0 +1,176 @@
+"""MI355X (gfx950) k-means assignment: Python binding of ``libkmeans_mi355x.so``.
+
+The functions here only marshal torch tensors into the C ABI declared in
+``include/kmeans_mi355x.h`` (device pointers, sizes, the current HIP stream);
+every step of the computation runs in the library's HIP kernels.  There is no
+CPU fallback: if the library is missing, the first call raises.
+
+    norms = kmeans_centroid_norms(C)                    # fp32 [K]
+    labels, min_dist = kmeans_assign(X, C, norms)       # int32 [N], fp32 [N]
+
+``X`` and ``C`` are ``torch.bfloat16`` CUDA tensors of shape ``[N, D]`` and
+``[K, D]``, contiguous.  Calls are asynchronous on the current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libkmeans_mi355x.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "kmeans_mi355x.h")
+
+KMEANS_OK = 0
+KMEANS_ERR_INVALID_ARG = 1
+KMEANS_ERR_UNSUPPORTED = 2
+KMEANS_ERR_ALIGNMENT = 3
+KMEANS_ERR_HIP = 4
+KMEANS_ERR_NO_MEMORY = 5
+
+PATH_AUTO = 0
+PATH_DIRECT = 1
+PATH_SPLIT = 2
+
+_STATUS_NAMES = {
+    0: "KMEANS_OK", 1: "KMEANS_ERR_INVALID_ARG", 2: "KMEANS_ERR_UNSUPPORTED",
+    3: "KMEANS_ERR_ALIGNMENT", 4: "KMEANS_ERR_HIP", 5: "KMEANS_ERR_NO_MEMORY",
+}
+
+_lib = None
+
+
+class KmeansError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIBRARY):
+    """Load the HIP library (after torch, so both use one HIP runtime)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is not built; run `python -m "
+            "means_nearest_centroid_amd.build` (or __graft_entry__.build())")
+    try:
+        import torch  # noqa: F401  -- maps torch's libamdhip64 first
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.kmeans_centroid_norms.argtypes = [vp, i64, i64, vp, vp]
+    lib.kmeans_centroid_norms.restype = ctypes.c_int
+    lib.kmeans_assign.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.kmeans_assign.restype = ctypes.c_int
+    lib.kmeans_assign_path.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp]
+    lib.kmeans_assign_path.restype = ctypes.c_int
+    lib.kmeans_plan.argtypes = [i64, i64, i64, i32p, i32p, i32p, i32p, i32p, i32p]
+    lib.kmeans_plan.restype = ctypes.c_int
+    lib.kmeans_last_error.argtypes = []
+    lib.kmeans_last_error.restype = ctypes.c_char_p
+    lib.kmeans_abi_version.argtypes = []
+    lib.kmeans_abi_version.restype = ctypes.c_int
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != KMEANS_OK:
+        raise KmeansError(status, lib.kmeans_last_error().decode(errors="replace"))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _matrix(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D torch.bfloat16 CUDA tensor "
+                         f"(got {t.dtype}, {tuple(t.shape)}, {t.device})")
+    return t
+
+
+def abi_version() -> int:
+    return load_library().kmeans_abi_version()
+
+
+def kmeans_plan(N: int, D: int, K: int) -> dict:
+    """Launch plan the library would use for a shape (no GPU needed)."""
+    lib = load_library()
+    vals = [ctypes.c_int32(0) for _ in range(6)]
+    _check(lib, lib.kmeans_plan(N, D, K, *[ctypes.byref(v) for v in vals]))
+    keys = ("path", "splits", "workgroups", "points_per_wg", "k_block", "padded_d")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def kmeans_centroid_norms(C, norms=None, stream=None):
+    """``norms[k] = sum_j C[k, j]**2`` (fp32), asynchronously on ``stream``."""
+    import torch
+    C = _matrix(C, "C")
+    K, D = C.shape
+    if norms is None:
+        norms = torch.empty(K, dtype=torch.float32, device=C.device)
+    lib = load_library()
+    _check(lib, lib.kmeans_centroid_norms(_ptr(C), K, D, _ptr(norms), _stream_handle(stream)))
+    return norms
+
+
+def _assign_args(X, C, norms, labels, min_dist):
+    import torch
+    X = _matrix(X, "X")
+    C = _matrix(C, "C")
+    N, D = X.shape
+    K = C.shape[0]
+    if C.shape[1] != D:
+        raise ValueError(f"X has D={D} but C has D={C.shape[1]}")
+    if (not isinstance(norms, torch.Tensor) or norms.dtype != torch.float32
+            or not norms.is_cuda or norms.numel() != K or not norms.is_contiguous()):
+        raise ValueError("norms must be a contiguous fp32 CUDA tensor of K elements")
+    if labels is None:
+        labels = torch.empty(N, dtype=torch.int32, device=X.device)
+    if min_dist is None:
+        min_dist = torch.empty(N, dtype=torch.float32, device=X.device)
+    return X, C, norms, N, D, K, labels, min_dist
+
+
+def kmeans_assign(X, C, norms, labels=None, min_dist=None, stream=None):
+    """Nearest centroid per point: ``(labels int32 [N], min_dist fp32 [N])``."""
+    X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
+    lib = load_library()
+    _check(lib, lib.kmeans_assign(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
+                                  _ptr(min_dist), _stream_handle(stream)))
+    return labels, min_dist
+
+
+def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, splits: int = 0,
+                       labels=None, min_dist=None, stream=None):
+    """``kmeans_assign`` with a forced path (``PATH_DIRECT`` / ``PATH_SPLIT``)."""
+    X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
+    lib = load_library()
+    _check(lib, lib.kmeans_assign_path(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
+                                       _ptr(min_dist), path, splits, _stream_handle(stream)))
+    return labels, min_dist
+
+
+def assign(X, C, norms=None):
+    """Convenience: compute the norms if not given, then assign."""
+    if norms is None:
+        norms = kmeans_centroid_norms(C)
+    return kmeans_assign(X, C, norms)

@@ -1,0 +1,183 @@
+// kmeans_api.hip -- the C ABI: argument validation, dispatch, launches.
+// Every check happens on the host before the first HIP call.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kmeans_internal.h"
+#include "kmeans_mi355x.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kmeans_status_t fail(kmeans_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kmeans_status_t ok() {
+    g_last_error.clear();
+    return KMEANS_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxRows = 0x7fffffffLL - 1024;   // int32 indexing headroom
+
+kmeans_status_t check_d(int64_t D) {
+    if (D < KMEANS_MIN_D || D > KMEANS_MAX_D || D % 16 != 0)
+        return fail(KMEANS_ERR_UNSUPPORTED,
+                    "D=%lld unsupported: need %d <= D <= %d and D %% 16 == 0",
+                    static_cast<long long>(D), KMEANS_MIN_D, KMEANS_MAX_D);
+    return KMEANS_OK;
+}
+
+kmeans_status_t check_shape(int64_t N, int64_t D, int64_t K) {
+    if (N < 0)
+        return fail(KMEANS_ERR_INVALID_ARG, "N=%lld must be >= 0", static_cast<long long>(N));
+    if (K < 1)
+        return fail(KMEANS_ERR_INVALID_ARG, "K=%lld must be >= 1", static_cast<long long>(K));
+    kmeans_status_t st = check_d(D);
+    if (st != KMEANS_OK)
+        return st;
+    if (N > kMaxRows || K > kMaxRows)
+        return fail(KMEANS_ERR_UNSUPPORTED, "N=%lld or K=%lld too large (max %lld)",
+                    static_cast<long long>(N), static_cast<long long>(K),
+                    static_cast<long long>(kMaxRows));
+    return KMEANS_OK;
+}
+
+kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int64_t N,
+                           int64_t D, int64_t K, int32_t *labels, float *min_dist,
+                           int path, int splits, hipStream_t stream) {
+    kmeans_status_t st = check_shape(N, D, K);
+    if (st != KMEANS_OK)
+        return st;
+    if (path < KMEANS_PATH_AUTO || path > KMEANS_PATH_SPLIT)
+        return fail(KMEANS_ERR_INVALID_ARG, "path=%d unknown", path);
+    if (splits < 0)
+        return fail(KMEANS_ERR_INVALID_ARG, "splits=%d must be >= 0", splits);
+    if (N == 0)
+        return ok();
+    if (!X || !C || !norms || !labels || !min_dist)
+        return fail(KMEANS_ERR_INVALID_ARG, "null pointer argument (X=%p C=%p norms=%p "
+                    "labels=%p min_dist=%p)", X, C, static_cast<const void *>(norms),
+                    static_cast<void *>(labels), static_cast<void *>(min_dist));
+    if (!aligned(X, 16) || !aligned(C, 16))
+        return fail(KMEANS_ERR_ALIGNMENT, "X and C must be 16-byte aligned");
+    if (!aligned(norms, 4) || !aligned(labels, 4) || !aligned(min_dist, 4))
+        return fail(KMEANS_ERR_ALIGNMENT, "norms, labels and min_dist must be 4-byte aligned");
+
+    const kmeans::Plan pl = kmeans::make_plan(N, D, K, path, splits);
+    const auto *Xb = static_cast<const uint16_t *>(X);
+    const auto *Cb = static_cast<const uint16_t *>(C);
+    const int n = static_cast<int>(N), d = static_cast<int>(D), k = static_cast<int>(K);
+
+    if (pl.path == KMEANS_PATH_DIRECT) {
+        hipError_t e = kmeans::launch_assign(pl, Xb, Cb, norms, n, d, k, labels, min_dist,
+                                             nullptr, nullptr, nullptr, stream);
+        if (e != hipSuccess)
+            return fail(KMEANS_ERR_HIP, "assign launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+
+    // Split path: stream-ordered scratch for the partial winners and ||x||^2.
+    const size_t per = static_cast<size_t>(N);
+    const size_t bytes = per * pl.splits * (sizeof(float) + sizeof(int32_t)) + per * sizeof(float);
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess || ws == nullptr)
+        return fail(KMEANS_ERR_NO_MEMORY, "hipMallocAsync(%zu) failed: %s", bytes,
+                    hipGetErrorString(e));
+    auto *ws_score = static_cast<float *>(ws);
+    auto *ws_label = reinterpret_cast<int32_t *>(ws_score + per * pl.splits);
+    auto *ws_xx = reinterpret_cast<float *>(ws_label + per * pl.splits);
+    e = kmeans::launch_assign(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score, ws_label,
+                              ws_xx, stream);
+    if (e == hipSuccess)
+        e = kmeans::launch_merge(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score,
+                                 ws_label, ws_xx, stream);
+    hipError_t ef = hipFreeAsync(ws, stream);
+    if (e != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "split-path launch failed: %s", hipGetErrorString(e));
+    if (ef != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "hipFreeAsync failed: %s", hipGetErrorString(ef));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kmeans_status_t kmeans_centroid_norms(const void *C, int64_t K, int64_t D, float *norms,
+                                      hipStream_t stream) {
+    if (K < 0)
+        return fail(KMEANS_ERR_INVALID_ARG, "K=%lld must be >= 0", static_cast<long long>(K));
+    kmeans_status_t st = check_d(D);
+    if (st != KMEANS_OK)
+        return st;
+    if (K > kMaxRows)
+        return fail(KMEANS_ERR_UNSUPPORTED, "K=%lld too large", static_cast<long long>(K));
+    if (K == 0)
+        return ok();
+    if (!C || !norms)
+        return fail(KMEANS_ERR_INVALID_ARG, "null pointer argument (C=%p norms=%p)", C,
+                    static_cast<void *>(norms));
+    if (!aligned(C, 16))
+        return fail(KMEANS_ERR_ALIGNMENT, "C must be 16-byte aligned");
+    if (!aligned(norms, 4))
+        return fail(KMEANS_ERR_ALIGNMENT, "norms must be 4-byte aligned");
+    hipError_t e = kmeans::launch_norms(static_cast<const uint16_t *>(C), static_cast<int>(K),
+                                        static_cast<int>(D), norms, stream);
+    if (e != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "norms launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms, int64_t N,
+                              int64_t D, int64_t K, int32_t *labels, float *min_dist,
+                              hipStream_t stream) {
+    return run_assign(X, C, norms, N, D, K, labels, min_dist, KMEANS_PATH_AUTO, 0, stream);
+}
+
+kmeans_status_t kmeans_assign_path(const void *X, const void *C, const float *norms,
+                                   int64_t N, int64_t D, int64_t K, int32_t *labels,
+                                   float *min_dist, int32_t path, int32_t splits,
+                                   hipStream_t stream) {
+    return run_assign(X, C, norms, N, D, K, labels, min_dist, path, splits, stream);
+}
+
+kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t *path, int32_t *splits,
+                            int32_t *workgroups, int32_t *points_per_wg, int32_t *k_block,
+                            int32_t *padded_d) {
+    kmeans_status_t st = check_shape(N, D, K);
+    if (st != KMEANS_OK)
+        return st;
+    const kmeans::Plan pl = kmeans::make_plan(N > 0 ? N : 1, D, K, KMEANS_PATH_AUTO, 0);
+    if (path)
+        *path = pl.path;
+    if (splits)
+        *splits = pl.splits;
+    if (workgroups)
+        *workgroups = N > 0 ? pl.wgs : 0;
+    if (points_per_wg)
+        *points_per_wg = pl.ppw;
+    if (k_block)
+        *k_block = pl.bk;
+    if (padded_d)
+        *padded_d = pl.ks * 16;
+    return ok();
+}
+
+const char *kmeans_last_error(void) { return g_last_error.c_str(); }
+
+int kmeans_abi_version(void) { return KMEANS_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// kmeans_internal.h -- launch plan and launchers shared by the C ABI layer
+// and the kernel translation unit.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kmeans {
+
+constexpr int kThreads = 256;        // 4 wave64s per workgroup, one per SIMD
+constexpr int kWavesPerWg = 4;
+constexpr int kTileRows = 32;        // centroid rows per MFMA tile (A operand)
+constexpr int kTileCols = 32;        // points per MFMA tile (B operand)
+constexpr int kMaxSplits = 64;
+constexpr int32_t kNoLabel = 0x7fffffff;
+
+// Kernel shape for a padded feature width of 16*ks (ks a power of two).
+constexpr int point_blocks_per_wave(int ks) { return ks <= 8 ? 2 : 1; }
+constexpr int k_block_rows(int ks) { return (512 / ks) > 32 ? (512 / ks) : 32; }
+constexpr int points_per_wg(int ks) { return kWavesPerWg * point_blocks_per_wave(ks) * kTileCols; }
+
+struct Plan {
+    int path;          // 1 direct, 2 split (same numbering as kmeans_path_t)
+    int splits;        // K-ranges (grid.y)
+    int ks;            // padded D / 16
+    int wgs;           // workgroups along N (grid.x)
+    int ppw;           // points per workgroup
+    int bk;            // centroid rows per LDS block
+    int k_chunk;       // centroids per K-range, multiple of bk
+};
+
+// force_path: 0 auto, 1 direct, 2 split; force_splits: 0 auto.
+// Requires 1 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller).
+Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_splits);
+
+hipError_t launch_norms(const uint16_t *C, int K, int D, float *norms, hipStream_t stream);
+
+// Direct path when ws_score == nullptr, otherwise writes per-split partial
+// winners to the workspace and the merge kernel finishes.
+hipError_t launch_assign(const Plan &plan, const uint16_t *X, const uint16_t *C,
+                         const float *norms, int N, int D, int K, int32_t *labels,
+                         float *min_dist, float *ws_score, int32_t *ws_label,
+                         float *ws_xx, hipStream_t stream);
+
+hipError_t launch_merge(const Plan &plan, const uint16_t *X, const uint16_t *C,
+                        const float *norms, int N, int D, int K, int32_t *labels,
+                        float *min_dist, const float *ws_score, const int32_t *ws_label,
+                        const float *ws_xx, hipStream_t stream);
+
+}  // namespace kmeans

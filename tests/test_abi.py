@@ -1,0 +1,132 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import means_nearest_centroid_amd as km
+from means_nearest_centroid_amd import build as kbuild
+
+
+@pytest.fixture(scope="module")
+def lib():
+    srcs = kbuild.SOURCES + [os.path.join(kbuild.CSRC, "kmeans_internal.h"), km.HEADER]
+    if not os.path.exists(km.LIBRARY) or any(
+            os.path.getmtime(s) > os.path.getmtime(km.LIBRARY) for s in srcs):
+        kbuild.build()
+    return km.load_library()
+
+
+def declared_functions():
+    text = open(km.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kmeans_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("kmeans_centroid_norms", "kmeans_assign", "kmeans_assign_path",
+              "kmeans_plan", "kmeans_last_error", "kmeans_abi_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+
+
+def test_abi_version(lib):
+    m = re.search(r"#define\s+KMEANS_ABI_VERSION\s+(\d+)", open(km.HEADER).read())
+    assert lib.kmeans_abi_version() == int(m.group(1))
+
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x10002)    # 2-byte aligned only
+NUL = ctypes.c_void_p(0)
+
+
+def assign_status(lib, X=FAKE, C=FAKE, n=FAKE, N=10, D=64, K=5, lab=FAKE, md=FAKE):
+    return lib.kmeans_assign(X, C, n, N, D, K, lab, md, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), km.KMEANS_ERR_INVALID_ARG),
+    (dict(K=0), km.KMEANS_ERR_INVALID_ARG),
+    (dict(K=-3), km.KMEANS_ERR_INVALID_ARG),
+    (dict(D=40), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(D=8), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(D=528), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(D=0), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(N=1 << 31), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(K=1 << 31), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(X=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(C=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(n=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(lab=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(md=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(X=FAKE_ODD), km.KMEANS_ERR_ALIGNMENT),
+    (dict(C=FAKE_ODD), km.KMEANS_ERR_ALIGNMENT),
+    (dict(n=FAKE_ODD), km.KMEANS_ERR_ALIGNMENT),
+    (dict(md=FAKE_ODD), km.KMEANS_ERR_ALIGNMENT),
+])
+def test_assign_rejects_bad_arguments(lib, kw, status):
+    assert assign_status(lib, **kw) == status
+    assert lib.kmeans_last_error().decode()
+
+
+def test_assign_empty_is_noop(lib):
+    # N == 0 returns before touching any pointer or the HIP runtime.
+    assert assign_status(lib, X=NUL, C=NUL, n=NUL, lab=NUL, md=NUL, N=0) == km.KMEANS_OK
+    assert lib.kmeans_last_error().decode() == ""
+
+
+def test_assign_path_rejects_bad_plan(lib):
+    st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 64, 5, FAKE, FAKE, 7, 0, NUL)
+    assert st == km.KMEANS_ERR_INVALID_ARG
+    st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 64, 5, FAKE, FAKE, 2, -1, NUL)
+    assert st == km.KMEANS_ERR_INVALID_ARG
+
+
+def test_norms_rejects_bad_arguments(lib):
+    f = lib.kmeans_centroid_norms
+    assert f(FAKE, -1, 64, FAKE, NUL) == km.KMEANS_ERR_INVALID_ARG
+    assert f(FAKE, 5, 24, FAKE, NUL) == km.KMEANS_ERR_UNSUPPORTED
+    assert f(NUL, 5, 64, FAKE, NUL) == km.KMEANS_ERR_INVALID_ARG
+    assert f(FAKE, 5, 64, NUL, NUL) == km.KMEANS_ERR_INVALID_ARG
+    assert f(FAKE_ODD, 5, 64, FAKE, NUL) == km.KMEANS_ERR_ALIGNMENT
+    assert f(NUL, 0, 64, NUL, NUL) == km.KMEANS_OK
+
+
+def test_plan_for_the_workloads(lib):
+    from means_nearest_centroid_amd.workloads import CONFIGS
+    plans = {i: km.kmeans_plan(c["N"], c["D"], c["K"]) for i, c in CONFIGS.items()}
+    for i in (3, 4, 5):
+        assert plans[i]["path"] == km.PATH_DIRECT and plans[i]["splits"] == 1
+    assert plans[2]["path"] == km.PATH_SPLIT and plans[2]["splits"] > 1
+    for i, c in CONFIGS.items():
+        p = plans[i]
+        assert p["padded_d"] >= c["D"] and p["padded_d"] % 16 == 0
+        assert p["workgroups"] * p["points_per_wg"] >= c["N"]
+        assert p["splits"] * p["k_block"] >= 1
+
+
+@pytest.mark.parametrize("N,D,K", [(1, 16, 1), (100, 80, 7), (5000, 192, 3000),
+                                   (70000, 512, 100000), (1 << 20, 64, 64)])
+def test_plan_covers_every_point_and_centroid(lib, N, D, K):
+    p = km.kmeans_plan(N, D, K)
+    assert p["workgroups"] * p["points_per_wg"] >= N
+    assert p["padded_d"] >= D and (p["padded_d"] & (p["padded_d"] - 1)) == 0
+    assert 1 <= p["splits"] <= 64
+    assert p["path"] in (km.PATH_DIRECT, km.PATH_SPLIT)
+    if p["path"] == km.PATH_DIRECT:
+        assert p["splits"] == 1
+
+
+def test_plan_rejects_bad_shapes(lib):
+    with pytest.raises(km.KmeansError):
+        km.kmeans_plan(10, 72, 5)
+    with pytest.raises(km.KmeansError):
+        km.kmeans_plan(10, 64, 0)

@@ -1,0 +1,302 @@
+"""HIP path against the fp64 oracle, through the C ABI, on an MI355X.
+
+Small shapes (ragged in N, K and D, spanning several tiles) are checked on
+every point; the five workloads run at their full sizes with the production
+dispatch and are checked on every point (workloads 1-2) or on a sample of
+points plus every structured point (3-5).  Acceptance rule: ``parity.py``.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import parity
+from means_nearest_centroid_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+km = pytest.importorskip("means_nearest_centroid_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    km.load_library()           # raises if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run(X, C, path=km.PATH_AUTO, splits=0):
+    Xd, Cd = dev(X), dev(C)
+    n = km.kmeans_centroid_norms(Cd)
+    lab, md = km.kmeans_assign_path(Xd, Cd, n, path, splits)
+    torch.cuda.synchronize()
+    return lab.cpu().numpy(), md.cpu().numpy()
+
+
+def test_native_library_is_loaded():
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert os.path.realpath(km.LIBRARY) in maps, "HIP library not mapped"
+    hip = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(hip) == 1, f"more than one HIP runtime mapped: {hip}"
+
+
+@pytest.mark.parametrize("K,D", [(1, 16), (37, 64), (300, 128), (129, 256), (70, 512),
+                                 (5000, 80), (33, 192)])
+def test_norms(K, D):
+    _, C, _ = W.gaussian_mixture(1, D, K, 5)
+    got = km.kmeans_centroid_norms(dev(C)).cpu().numpy().astype(np.float64)
+    ref = oracle.centroid_norms(C)
+    assert np.allclose(got, ref, rtol=2e-6, atol=1e-6)
+    C2 = C.copy()
+    C2[-1] = C2[0]
+    g2 = km.kmeans_centroid_norms(dev(C2)).cpu().numpy()
+    assert g2[-1].tobytes() == g2[0].tobytes(), "identical rows, different norms"
+
+
+SMALL = [  # (N, D, K): ragged tails in every dimension, several tiles
+    (4133, 64, 275), (1000, 16, 37), (777, 128, 300), (2050, 256, 129),
+    (513, 512, 70), (300, 80, 45), (64, 32, 1), (1, 16, 5), (257, 48, 1000),
+    (3000, 128, 2049),
+]
+
+
+@pytest.mark.parametrize("path", [km.PATH_AUTO, km.PATH_DIRECT, km.PATH_SPLIT],
+                         ids=["auto", "direct", "split"])
+@pytest.mark.parametrize("N,D,K", SMALL)
+def test_small_shapes(N, D, K, path):
+    X, C, _ = W.gaussian_mixture(N, D, K, 1000 + N + K)
+    lab, md = run(X, C, path)
+    parity.check(X, C, lab, md)
+
+
+@pytest.mark.parametrize("seed", W.SEEDS)
+def test_workload1_full(seed):
+    X, C, _ = W.make_config(1, seed)
+    lab, md = run(X, C)
+    st = parity.check(X, C, lab, md)
+    assert st["bad_strict"] == 0
+
+
+def test_workload2_full():
+    X, C, _ = W.make_config(2, 17)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md)
+
+
+@pytest.mark.parametrize("seed", [29, 43])
+def test_workload2_sampled(seed):
+    X, C, _ = W.make_config(2, seed)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md, idx=parity.sample_indices(X.shape[0], seed, 1024, 1024))
+
+
+@pytest.mark.parametrize("seed", W.SEEDS)
+def test_workload3_sampled(seed):
+    X, C, _ = W.make_config(3, seed)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md, idx=parity.sample_indices(X.shape[0], seed, 1024, 1024))
+
+
+def test_workload4_sampled():
+    X, C, _ = W.make_config(4, 17)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md, idx=parity.sample_indices(X.shape[0], 4, 1024, 1024))
+
+
+@pytest.fixture(scope="module")
+def workload5():
+    X, C, meta = W.make_config(5, 17)
+    lab, md = run(X, C)
+    return X, C, meta, lab, md
+
+
+def test_workload5_sampled(workload5):
+    X, C, meta, lab, md = workload5
+    N = X.shape[0]
+    parity.check(X, C, lab, md, idx=parity.sample_indices(N, 5, 0, 2048, 4096 + 64))
+
+
+def test_workload5_nan_slice(workload5):
+    X, C, meta, lab, md = workload5
+    parity.check(X, C, lab, md, idx=meta["nan_slice"])
+
+
+def test_workload5_dyadic_ties_bit_exact(workload5):
+    X, C, meta, lab, md = workload5
+    idx = meta["dyadic_points"]
+    assert np.array_equal(lab[idx], meta["dyadic_labels"])
+    assert np.array_equal(md[idx].astype(np.float64), meta["dyadic_sqdist"])
+
+
+def test_workload5_duplicates_and_equal_rows(workload5):
+    X, C, meta, lab, md = workload5
+    for s, t in meta["dup_pairs"]:
+        assert not np.any(lab == t), f"duplicate row {t} beat its copy {s}"
+    eq = meta["equal_rows"]
+    assert not np.any(np.isin(lab, eq[1:])), "a non-lowest equal row won"
+    near_eq = np.flatnonzero(np.isin(meta["generating_centre"], eq))
+    near_eq = near_eq[near_eq >= W.NAN_SLICE_POINTS]
+    assert len(near_eq) > 0
+    parity.check(X, C, lab, md, idx=near_eq)
+    srcs = meta["dup_pairs"][:, 0]
+    near_dup = np.flatnonzero(np.isin(meta["generating_centre"], srcs))
+    near_dup = near_dup[near_dup >= W.NAN_SLICE_POINTS][:2048]
+    assert len(near_dup) > 0
+    parity.check(X, C, lab, md, idx=near_dup)
+
+
+def test_nonfinite_centroids():
+    X, C, _ = W.gaussian_mixture(700, 64, 300, 77)
+    C[3, 5] = W.BF16_QNAN
+    C[40, 7] = W.BF16_PINF
+    C[41, 9] = W.BF16_NINF
+    C[299, 0] = W.BF16_PINF
+    X[10, 3] = W.BF16_PINF
+    X[11, 4] = W.BF16_NINF
+    X[12, 5] = W.BF16_QNAN
+    for path in (km.PATH_DIRECT, km.PATH_SPLIT):
+        lab, md = run(X, C, path)
+        parity.check(X, C, lab, md)
+
+
+def test_all_scores_infinite_or_nan():
+    """Every score +inf or NaN: lowest +inf index wins, else 0 (cold path)."""
+    D = 32
+    x = np.zeros((3, D), np.uint16)
+    x[:, 0] = W.dyadic_to_bf16_bits(np.array([-1]), 0)[0]
+    x[2, 1] = W.BF16_QNAN
+    C = np.zeros((70, D), np.uint16)
+    C[:, 0] = W.BF16_PINF             # x_0 = -1: score +inf for every row
+    C[0, 2] = W.BF16_QNAN             # row 0: NaN score
+    C[1, 1] = W.BF16_NINF             # row 1 with x_1 = 0: inf*0 -> NaN
+    lab, md = run(x, C, km.PATH_DIRECT)
+    lab2, md2 = run(x, C, km.PATH_SPLIT, 2)
+    assert lab[0] == 2 and lab[1] == 2 and lab[2] == 0
+    assert np.isinf(md[0]) and np.isnan(md[2])
+    assert np.array_equal(lab, lab2)
+    parity.check(x, C, lab, md)
+
+
+def test_zero_and_signed_zero_points():
+    X, C, _ = W.gaussian_mixture(200, 64, 100, 78)
+    X[0] = W.BF16_PZERO
+    X[1] = W.BF16_NZERO
+    X[2, ::2] = W.BF16_NZERO
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md)
+    assert lab[0] == lab[1]
+
+
+def test_single_centroid():
+    X, C, _ = W.gaussian_mixture(1000, 128, 1, 79)
+    lab, md = run(X, C)
+    assert np.all(lab == 0)
+    parity.check(X, C, lab, md)
+
+
+def test_empty_input():
+    C = dev(W.gaussian_mixture(1, 64, 10, 80)[1])
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    n = km.kmeans_centroid_norms(C)
+    lab, md = km.kmeans_assign(X, C, n)
+    torch.cuda.synchronize()
+    assert lab.numel() == 0 and md.numel() == 0
+
+
+def test_maximum_d_and_large_k():
+    X, C, _ = W.gaussian_mixture(600, 512, 3000, 81)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md)
+
+
+def test_large_k_small_n():
+    X, C, _ = W.gaussian_mixture(300, 64, 70000, 82)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md)
+
+
+# ---------------------------------------------------------------- metamorphic
+
+@pytest.mark.parametrize("N,D,K", [(5000, 64, 4096), (20000, 128, 1000), (3000, 256, 777)])
+def test_split_equals_direct_bitwise(N, D, K):
+    X, C, _ = W.gaussian_mixture(N, D, K, 90 + D)
+    ld, md_d = run(X, C, km.PATH_DIRECT)
+    for splits in (0, 2, 3, 7):
+        ls, md_s = run(X, C, km.PATH_SPLIT, splits)
+        assert np.array_equal(ld, ls)
+        assert md_d.tobytes() == md_s.tobytes()
+
+
+def test_deterministic_repeat():
+    X, C, _ = W.make_config(2, 29)
+    a = run(X, C)
+    b = run(X, C)
+    assert np.array_equal(a[0], b[0]) and a[1].tobytes() == b[1].tobytes()
+
+
+def test_point_permutation_bitwise():
+    X, C, _ = W.gaussian_mixture(9000, 128, 700, 91)
+    lab, md = run(X, C)
+    perm = np.random.default_rng(1).permutation(X.shape[0])
+    lp, mp = run(X[perm], C)
+    assert np.array_equal(lab[perm], lp) and md[perm].tobytes() == mp.tobytes()
+
+
+def test_centroid_permutation():
+    X, C, _ = W.gaussian_mixture(9000, 64, 700, 92)
+    lab, md = run(X, C)
+    perm = np.random.default_rng(2).permutation(C.shape[0])
+    lp, mp = run(X, C[perm])
+    ref = oracle.assign(X, C)
+    with np.errstate(invalid="ignore"):
+        strict = (ref["second"] - ref["best"]) >= 1e-3 * (np.abs(ref["best"]) + 1)
+    # label j under C[perm] is original row perm[j]
+    assert np.array_equal(perm[lp][strict], lab[strict])
+    assert md[strict].tobytes() == mp[strict].tobytes()
+
+
+@pytest.mark.parametrize("a", [-4, 3])
+def test_power_of_two_scaling_bitwise(a):
+    X, C, _ = W.gaussian_mixture(4000, 128, 500, 93)
+    lab, md = run(X, C)
+    f = np.float32(2.0 ** a)
+    Xs = W.f32_to_bf16_bits(W.bf16_bits_to_f32(X) * f)
+    Cs = W.f32_to_bf16_bits(W.bf16_bits_to_f32(C) * f)
+    ls, ms = run(Xs, Cs)
+    assert np.array_equal(lab, ls)
+    assert np.array_equal(md.astype(np.float64) * 4.0 ** a, ms.astype(np.float64))
+
+
+def test_non_default_stream():
+    X, C, _ = W.gaussian_mixture(3000, 64, 500, 94)
+    Xd, Cd = dev(X), dev(C)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        n = km.kmeans_centroid_norms(Cd)
+        lab, md = km.kmeans_assign(Xd, Cd, n)
+    s.synchronize()
+    parity.check(X, C, lab.cpu().numpy(), md.cpu().numpy())
+
+
+def test_api_errors_on_device_tensors():
+    C = dev(W.gaussian_mixture(1, 64, 10, 95)[1])
+    X = dev(W.gaussian_mixture(33, 64, 10, 95)[0])
+    n = km.kmeans_centroid_norms(C)
+    bad = X.view(-1)[1:1 + 32 * 64].view(32, 64)   # 2-byte offset
+    with pytest.raises(km.KmeansError) as e:
+        km.kmeans_assign(bad, C, n)
+    assert e.value.status == km.KMEANS_ERR_ALIGNMENT
+    Xw = dev(W.gaussian_mixture(8, 40, 10, 95)[0])
+    Cw = dev(W.gaussian_mixture(1, 40, 10, 95)[1])
+    with pytest.raises(km.KmeansError) as e:
+        km.kmeans_centroid_norms(Cw)
+    assert e.value.status == km.KMEANS_ERR_UNSUPPORTED

@@ -16,7 +16,9 @@ constexpr int32_t kNoLabel = 0x7fffffff;
 
 // Kernel shape for a padded feature width of 16*ks (ks a power of two).
 constexpr int point_blocks_per_wave(int ks) { return ks <= 8 ? 2 : 1; }
-constexpr int k_block_rows(int ks) { return (512 / ks) > 32 ? (512 / ks) : 32; }
+// Centroid rows per LDS block: a whole, even number of 32-row tiles, at most
+// one norm per thread, and a multiple of 256 16-byte chunks.
+constexpr int k_block_rows(int ks) { return ks <= 2 ? 256 : (ks == 4 ? 128 : 64); }
 constexpr int points_per_wg(int ks) { return kWavesPerWg * point_blocks_per_wave(ks) * kTileCols; }
 
 struct Plan {

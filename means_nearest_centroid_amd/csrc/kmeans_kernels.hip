@@ -17,12 +17,20 @@
 //    norms" / "Barrier elimination" rows reach the same goal on Blackwell).
 //  * Points stay resident in VGPRs for the whole K loop; centroid blocks are
 //    double-buffered through LDS with an XOR swizzle so the A-operand reads
-//    (ds_read_b128, 32 rows at one column) hit distinct banks.
-//  * The epilogue keeps two running (score, index) chains per point (even and
-//    odd accumulator slots, the pages' "Two-chain argmin"), each scanned in
-//    increasing index with a strict '<', merged by (score, index) at the end,
-//    then across the two lanes that share a point ("Deterministic winner
-//    merge").  The N x K score matrix never leaves registers.
+//    (ds_read_b128, 32 rows at one column) hit distinct banks.  Buffer loads
+//    return zero past the end, so ragged N, K and D need no branches.
+//  * Accumulators are double-buffered so the MFMAs of the next tile are in
+//    flight while the VALU reduces the current one.
+//  * The epilogue does not run one compare-select chain per score (the
+//    pages' serial scan and its "Two-chain argmin" ILP fix): on CDNA4 an
+//    index can only enter a v_cndmask as a VGPR or an inline constant, so a
+//    per-score (score, index) update costs 3+ VALU ops.  Instead each tile is
+//    reduced to its minimum with v_min3 (half an op per score) and the exact
+//    slot is searched only when that minimum beats the running best, which
+//    becomes rare once a point has seen its nearest centroids.  Ties keep the
+//    lower index at every level; the two lanes that share a point merge by
+//    (score, index) ("Deterministic winner merge").  The N x K score matrix
+//    never leaves registers.
 //  * A point whose every score is +inf or NaN, or whose result is not finite,
 //    takes a cold per-lane path after the loop (rule: -inf < finite < +inf <
 //    NaN, ties to the lower index).
@@ -120,8 +128,34 @@ __device__ void finalize_point(int n, float s, int32_t lab, float xx,
     min_dist[n] = md;
 }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads past the end
+// return zero, which pads ragged N, K and D without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past num_records
+
 // One workgroup = 4 waves; wave w owns P blocks of 32 points.  Grid:
 // x = point workgroups, y = K-ranges of k_chunk centroids.
+//
+// Hot loop, per wave: centroid tiles of 32 rows stream through LDS in blocks
+// of BK rows (two buffers, one barrier per block; block b+2 is fetched into
+// registers while block b is consumed).  Accumulators are double-buffered:
+// the MFMAs of tile t+1 are issued before the epilogue of tile t, so the
+// matrix pipe works while the VALU reduces.
+//
+// Epilogue per (tile, point block), per lane (16 scores of one point):
+//   m = min(best, s_0..s_15)           8 v_min3 (NaN inputs are ignored)
+//   if m < best (strict; rare after the first tiles):
+//       slot = lowest r with s_r == m  (inline-constant selects)
+//       best = m, best_tile = tile, best_slot = slot
+// m is always one of its inputs, so the winner is exact; a strict '<' keeps
+// the earlier tile on equal scores, and the slot search keeps the lower row.
 template <int KS, int P, int BK, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(WPE, WPE)))
@@ -132,10 +166,11 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                    int32_t *__restrict__ ws_label, float *__restrict__ ws_xx) {
     constexpr int S = 2 * KS;                  // 16-byte chunks per centroid row
     constexpr int ROW_BYTES = 16 * S;
+    constexpr int TB = BK / kTileRows;         // tiles per block
     constexpr int LOADS = BK * S / kThreads;   // chunks each thread stages per block
-    constexpr int NLOADS = (BK + kThreads - 1) / kThreads;
     static_assert((BK * S) % kThreads == 0, "block must split evenly");
-    static_assert(BK % kTileRows == 0, "block is whole tiles");
+    static_assert(TB % 2 == 0, "accumulator parity must restart at each block");
+    static_assert(BK <= kThreads, "one norm per thread");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][BK * ROW_BYTES];
     __shared__ __attribute__((aligned(16))) float lds_n[2][BK];
@@ -148,152 +183,166 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 
     const int split = blockIdx.y;
     const int k_begin = split * k_chunk;
-    const int k_end = min(K, k_begin + k_chunk);
-    const int point0 = blockIdx.x * (kWavesPerWg * P * kTileCols) + wave * (P * kTileCols);
+    const int k_rows = min(K, k_begin + k_chunk) - k_begin;
+    const int wg_point0 = blockIdx.x * (kWavesPerWg * P * kTileCols);
+    const int wg_points = min(N - wg_point0, kWavesPerWg * P * kTileCols);
+    const uint32_t row_bytes = static_cast<uint32_t>(D) * 2u;
 
     // ---- resident points: -2x as MFMA B fragments, and ||x||^2 ----
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + static_cast<size_t>(wg_point0) * D,
+                                                static_cast<uint32_t>(wg_points) * row_bytes);
     u32x4 xb[P][KS];
     float xx[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         xx[p] = 0.0f;
-        const int row = point0 + p * kTileCols + col;
+        const uint32_t prow = static_cast<uint32_t>((wave * P + p) * kTileCols + col);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int c0 = ks * 16 + half * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row < N && c0 < D)
-                v = *reinterpret_cast<const u32x4 *>(X + static_cast<size_t>(row) * D + c0);
-            xb[p][ks] = neg2_and_square(v, xx[p]);
+            const uint32_t off = c0 < D ? prow * row_bytes + c0 * 2 : kOutOfRange;
+            xb[p][ks] = neg2_and_square(load16(xr, off), xx[p]);
         }
         xx[p] += __shfl_xor(xx[p], 32);
     }
 
-    float bs[P][2];
-    int32_t bi[P][2];
+    // ---- staging of centroid blocks: buffer loads -> registers -> LDS ----
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(C + static_cast<size_t>(k_begin) * D,
+                                                static_cast<uint32_t>(k_rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t nr = make_rsrc(norms + k_begin, static_cast<uint32_t>(k_rows) * 4u);
+    uint32_t src_off[LOADS];
+    uint32_t dst_off[LOADS];
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-            bs[p][ch] = INFINITY;
-            bi[p][ch] = kNoLabel;
-        }
-
-    // ---- centroid blocks: global -> registers -> LDS, double-buffered ----
+    for (int i = 0; i < LOADS; ++i) {
+        const int q = tid + i * kThreads;
+        const int r = q / S, c = q % S;
+        src_off[i] = c * 8 < D ? static_cast<uint32_t>(r) * row_bytes + c * 16 : kOutOfRange;
+        dst_off[i] = r * ROW_BYTES + swz<S>(r, c) * 16;
+    }
     u32x4 stage[LOADS];
-    float nstage[NLOADS];
-    auto fetch = [&](int kb) {
+    float nstage = 0.0f;
+    auto fetch = [&](int blk) {
+        const uint32_t base = static_cast<uint32_t>(blk) * BK * row_bytes;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int q = tid + i * kThreads;
-            const int r = q / S, c = q % S;
-            const int k = kb + r;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (k < k_end && c * 8 < D)
-                v = *reinterpret_cast<const u32x4 *>(C + static_cast<size_t>(k) * D + c * 8);
-            stage[i] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < NLOADS; ++i) {
-            const int r = tid + i * kThreads;
+        for (int i = 0; i < LOADS; ++i)
+            stage[i] = load16(cr, src_off[i] == kOutOfRange ? kOutOfRange : src_off[i] + base);
+        if (tid < BK) {
+            const int r = blk * BK + tid;
+            const float v = __uint_as_float(static_cast<uint32_t>(
+                __builtin_amdgcn_raw_buffer_load_b32(nr, static_cast<uint32_t>(r) * 4u, 0, 0)));
             // Rows past the range score NaN, which never wins.
-            nstage[i] = (r < BK && kb + r < k_end) ? norms[kb + r] : __builtin_nanf("");
+            nstage = r < k_rows ? v : __builtin_nanf("");
         }
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int q = tid + i * kThreads;
-            const int r = q / S, c = q % S;
-            *reinterpret_cast<u32x4 *>(&lds_c[buf][r * ROW_BYTES + swz<S>(r, c) * 16]) = stage[i];
-        }
+        for (int i = 0; i < LOADS; ++i)
+            *reinterpret_cast<u32x4 *>(&lds_c[buf][dst_off[i]]) = stage[i];
+        if (tid < BK)
+            lds_n[buf][tid] = nstage;
+    };
+
+    // Per-lane LDS read offsets inside a tile (tiles start at multiples of 32
+    // rows, where the swizzle pattern repeats).
+    int a_off[KS];
 #pragma unroll
-        for (int i = 0; i < NLOADS; ++i) {
-            const int r = tid + i * kThreads;
-            if (r < BK)
-                lds_n[buf][r] = nstage[i];
+    for (int ks = 0; ks < KS; ++ks)
+        a_off[ks] = col * ROW_BYTES + swz<S>(col, 2 * ks + half) * 16;
+
+    auto tile_mfma = [&](int buf, int r0, f32x16 (&acc)[P]) {
+        f32x16 ninit;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(&lds_n[buf][r0 + 8 * q + 4 * half]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ninit[4 * q + e] = v[e];
+        }
+        bf16x8 a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a[ks] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds_c[buf][r0 * ROW_BYTES + a_off[ks]]));
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            acc[p] = ninit;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), acc[p], 0, 0, 0);
+    };
+
+    float bs[P];
+    int32_t bt[P], bo[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        bs[p] = INFINITY;
+        bt[p] = kNoLabel;
+        bo[p] = 0;
+    }
+    // acc[p][r] = s for centroid kt + 8*(r/4) + 4*half + r%4.
+    auto epilogue = [&](const f32x16 (&acc)[P], int kt) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            float m = bs[p];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2)
+                m = __builtin_fminf(__builtin_fminf(m, acc[p][r]), acc[p][r + 1]);
+            if (m < bs[p]) {
+                int slot = 0;
+#pragma unroll
+                for (int r = 15; r >= 0; --r)
+                    slot = acc[p][r] == m ? 8 * (r >> 2) + (r & 3) : slot;
+                bs[p] = m;
+                bt[p] = kt;
+                bo[p] = slot;
+            }
         }
     };
 
-    const int nblocks = (k_end - k_begin + BK - 1) / BK;
-    fetch(k_begin);
+    const int nblocks = (k_rows + BK - 1) / BK;
+    fetch(0);
     store(0);
     __syncthreads();
+    if (nblocks > 1)
+        fetch(1);
 
+    f32x16 acc0[P], acc1[P];
+    tile_mfma(0, 0, acc0);
     for (int b = 0; b < nblocks; ++b) {
         const int buf = b & 1;
         const int kb = k_begin + b * BK;
-        if (b + 1 < nblocks)
-            fetch(kb + BK);
-
 #pragma unroll
-        for (int tt = 0; tt < BK / kTileRows; ++tt) {
-            const int r0 = tt * kTileRows;
-            if (kb + r0 >= k_end)
-                break;
-            // Norm tile as the MFMA C input: slot r of this lane is row
-            // 8*(r/4) + 4*half + r%4 of the tile.
-            f32x16 ninit;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(&lds_n[buf][r0 + 8 * q + 4 * half]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ninit[4 * q + e] = v[e];
+        for (int j = 0; j < TB; ++j) {
+            f32x16(&cur)[P] = (j & 1) ? acc1 : acc0;
+            f32x16(&nxt)[P] = (j & 1) ? acc0 : acc1;
+            if (j + 1 < TB) {
+                tile_mfma(buf, (j + 1) * kTileRows, nxt);
+            } else if (b + 1 < nblocks) {
+                store(buf ^ 1);
+                __syncthreads();
+                if (b + 2 < nblocks)
+                    fetch(b + 2);
+                tile_mfma(buf ^ 1, 0, nxt);
             }
-            bf16x8 a[KS];
-            const int arow = r0 + col;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                a[ks] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(
-                                &lds_c[buf][arow * ROW_BYTES + swz<S>(arow, 2 * ks + half) * 16]));
-
-            const int kt = kb + r0;   // wave-uniform index base of this tile
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                f32x16 acc = ninit;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), acc, 0, 0, 0);
-                // acc[r] = s for centroid kt + 8*(r/4) + 4*half + r%4 (the
-                // lane term 4*half is added once after the loop).
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ch = r & 1;
-                    const int32_t idx = kt + 8 * (r >> 2) + (r & 3);
-                    const float s = acc[r];
-                    const bool lt = s < bs[p][ch];
-                    bs[p][ch] = lt ? s : bs[p][ch];
-                    bi[p][ch] = lt ? idx : bi[p][ch];
-                }
-            }
+            epilogue(cur, kb + j * kTileRows);
         }
-
-        if (b + 1 < nblocks)
-            store(buf ^ 1);
-        __syncthreads();
     }
 
-    // ---- merge chains, then the two lanes that hold the same point ----
+    // ---- merge the two lanes that hold the same point ----
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        float s = bs[p][0];
-        int32_t i = bi[p][0];
-        if (pair_before(bs[p][1], bi[p][1], s, i)) {
-            s = bs[p][1];
-            i = bi[p][1];
-        }
-        if (i != kNoLabel)
-            i += 4 * half;
+        float s = bs[p];
+        int32_t i = bt[p] == kNoLabel ? kNoLabel : bt[p] + bo[p] + 4 * half;
         const float so = __shfl_xor(s, 32);
         const int32_t io = __shfl_xor(i, 32);
         if (pair_before(so, io, s, i)) {
             s = so;
             i = io;
         }
-        const int n = point0 + p * kTileCols + col;
+        const int n = wg_point0 + (wave * P + p) * kTileCols + col;
         if (half == 0 && n < N) {
             if (write_partials) {
                 ws_score[static_cast<size_t>(split) * N + n] = s;

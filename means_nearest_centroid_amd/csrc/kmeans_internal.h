@@ -15,10 +15,11 @@ constexpr int kMaxSplits = 64;
 constexpr int32_t kNoLabel = 0x7fffffff;
 
 // Kernel shape for a padded feature width of 16*ks (ks a power of two).
-constexpr int point_blocks_per_wave(int ks) { return ks <= 8 ? 2 : 1; }
-// Centroid rows per LDS block: a whole, even number of 32-row tiles, at most
-// one norm per thread, and a multiple of 256 16-byte chunks.
-constexpr int k_block_rows(int ks) { return ks <= 2 ? 256 : (ks == 4 ? 128 : 64); }
+constexpr int point_blocks_per_wave(int ks) { return ks <= 4 ? 4 : (ks == 8 ? 2 : 1); }
+// Centroid rows per LDS block (one of two ring stages): whole 32-row tiles,
+// at most one norm per thread, about 32 KiB of centroid data (64 KiB at
+// D = 512, where one workgroup holds a CU).
+constexpr int k_block_rows(int ks) { return ks <= 4 ? 256 : (ks == 8 ? 128 : 64); }
 constexpr int points_per_wg(int ks) { return kWavesPerWg * point_blocks_per_wave(ks) * kTileCols; }
 
 struct Plan {

@@ -140,14 +140,36 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past num_records
 
+#define KM_LDS __attribute__((address_space(3)))
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane i writes dst + 16*i.  The builtin exists only for the device
+// target; clang's host pass (which emits the launch stubs and never runs
+// this body) drops the whole kernel if it sees it, hence the guard.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, KM_LDS void *dst, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+#endif
+}
+
 // One workgroup = 4 waves; wave w owns P blocks of 32 points.  Grid:
 // x = point workgroups, y = K-ranges of k_chunk centroids.
 //
-// Hot loop, per wave: centroid tiles of 32 rows stream through LDS in blocks
-// of BK rows (two buffers, one barrier per block; block b+2 is fetched into
-// registers while block b is consumed).  Accumulators are double-buffered:
-// the MFMAs of tile t+1 are issued before the epilogue of tile t, so the
-// matrix pipe works while the VALU reduces.
+// Data movement.  Centroid rows stream through two LDS stages in blocks of
+// BK rows.  Each block is copied global -> LDS by buffer_load ... lds (no
+// staging registers); its norms go through one register per thread.  One
+// barrier per block, at the start of the block's last tile, publishes the
+// next block; by then every wave has also finished reading the current
+// block's stage (the last tile's fragments were read one tile earlier), so
+// the DMA for the block after next goes into that stage right behind the
+// barrier and has a whole block of compute to land.  The two stages are
+// distinct arrays and the block loop is unrolled by two, so the compiler can
+// tell a ds_read of one stage from a DMA into the other and does not wait
+// on the DMA.
+//
+// Per tile (32 centroid rows) a wave issues P*KS MFMAs; right after the last
+// MFMA that reads A fragment ks, the fragment of the NEXT tile is read into
+// the same registers, so LDS latency hides behind the MFMA chain.
 //
 // Epilogue per (tile, point block), per lane (16 scores of one point):
 //   m = min(best, s_0..s_15)           8 v_min3 (NaN inputs are ignored)
@@ -167,13 +189,15 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     constexpr int S = 2 * KS;                  // 16-byte chunks per centroid row
     constexpr int ROW_BYTES = 16 * S;
     constexpr int TB = BK / kTileRows;         // tiles per block
-    constexpr int LOADS = BK * S / kThreads;   // chunks each thread stages per block
-    static_assert((BK * S) % kThreads == 0, "block must split evenly");
-    static_assert(TB % 2 == 0, "accumulator parity must restart at each block");
-    static_assert(BK <= kThreads, "one norm per thread");
+    constexpr int STAGE_BYTES = BK * ROW_BYTES;
+    constexpr int DMA_PER_WAVE = STAGE_BYTES / (1024 * kWavesPerWg);
+    static_assert(STAGE_BYTES % (1024 * kWavesPerWg) == 0, "block must split into 1 KiB DMAs");
+    static_assert(BK % kTileRows == 0 && BK <= kThreads, "block shape");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][BK * ROW_BYTES];
-    __shared__ __attribute__((aligned(16))) float lds_n[2][BK];
+    __shared__ __attribute__((aligned(16))) uint8_t c_st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t c_st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) float n_st0[BK];
+    __shared__ __attribute__((aligned(16))) float n_st1[BK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -206,40 +230,40 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         xx[p] += __shfl_xor(xx[p], 32);
     }
 
-    // ---- staging of centroid blocks: buffer loads -> registers -> LDS ----
+    // ---- centroid blocks: DMA into the LDS ring, norms via one register ----
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(C + static_cast<size_t>(k_begin) * D,
                                                 static_cast<uint32_t>(k_rows) * row_bytes);
     const __amdgpu_buffer_rsrc_t nr = make_rsrc(norms + k_begin, static_cast<uint32_t>(k_rows) * 4u);
-    uint32_t src_off[LOADS];
-    uint32_t dst_off[LOADS];
+    // Lane `lane` of DMA i writes LDS bytes [o, o+16) of the stage; fetch the
+    // global chunk that the swizzled layout puts there (XOR is its own inverse).
+    uint32_t dma_src[DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int q = tid + i * kThreads;
-        const int r = q / S, c = q % S;
-        src_off[i] = c * 8 < D ? static_cast<uint32_t>(r) * row_bytes + c * 16 : kOutOfRange;
-        dst_off[i] = r * ROW_BYTES + swz<S>(r, c) * 16;
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+        const int o = (wave * DMA_PER_WAVE + i) * 1024 + lane * 16;
+        const int r = o / ROW_BYTES, c = swz<S>(r, (o % ROW_BYTES) / 16);
+        dma_src[i] = c * 8 < D ? static_cast<uint32_t>(r) * row_bytes + c * 16 : kOutOfRange;
     }
-    u32x4 stage[LOADS];
-    float nstage = 0.0f;
-    auto fetch = [&](int blk) {
+    auto dma = [&](int blk, uint8_t *stage) {
         const uint32_t base = static_cast<uint32_t>(blk) * BK * row_bytes;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            stage[i] = load16(cr, src_off[i] == kOutOfRange ? kOutOfRange : src_off[i] + base);
+        for (int i = 0; i < DMA_PER_WAVE; ++i)
+            dma16(cr, (KM_LDS void *)(stage + (wave * DMA_PER_WAVE + i) * 1024),
+                  dma_src[i] == kOutOfRange ? kOutOfRange : dma_src[i] + base);
+    };
+    uint32_t nbits = 0;
+    bool nvalid = false;
+    auto load_norm = [&](int blk) {
         if (tid < BK) {
             const int r = blk * BK + tid;
-            const float v = __uint_as_float(static_cast<uint32_t>(
-                __builtin_amdgcn_raw_buffer_load_b32(nr, static_cast<uint32_t>(r) * 4u, 0, 0)));
-            // Rows past the range score NaN, which never wins.
-            nstage = r < k_rows ? v : __builtin_nanf("");
+            nbits = static_cast<uint32_t>(
+                __builtin_amdgcn_raw_buffer_load_b32(nr, static_cast<uint32_t>(r) * 4u, 0, 0));
+            nvalid = r < k_rows;
         }
     };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            *reinterpret_cast<u32x4 *>(&lds_c[buf][dst_off[i]]) = stage[i];
+    auto write_norm = [&](float *stage) {
+        // Rows past the range score NaN, which never wins.
         if (tid < BK)
-            lds_n[buf][tid] = nstage;
+            stage[tid] = nvalid ? __uint_as_float(nbits) : __builtin_nanf("");
     };
 
     // Per-lane LDS read offsets inside a tile (tiles start at multiples of 32
@@ -248,30 +272,39 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         a_off[ks] = col * ROW_BYTES + swz<S>(col, 2 * ks + half) * 16;
-
-    auto tile_mfma = [&](int buf, int r0, f32x16 (&acc)[P]) {
-        f32x16 ninit;
+    auto read_a = [&](const uint8_t *stage, int r0, int ks) {
+        return __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4 *>(&stage[r0 * ROW_BYTES + a_off[ks]]));
+    };
+    // Norm tile as the MFMA C input: slot r of this lane is tile row
+    // 8*(r/4) + 4*half + r%4.
+    auto read_n = [&](const float *stage, int r0) {
+        f32x16 v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(&lds_n[buf][r0 + 8 * q + 4 * half]);
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(&stage[r0 + 8 * q + 4 * half]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                ninit[4 * q + e] = v[e];
+                v[4 * q + e] = t[e];
         }
-        bf16x8 a[KS];
+        return v;
+    };
+
+    bf16x8 a[KS];
+    f32x16 ninit;
+    // MFMAs of the current tile (operands a, ninit); each operand register is
+    // refilled with the next tile's fragment right after its last use.
+    auto compute = [&](const uint8_t *next_c, const float *next_n, int next_r0, f32x16 (&acc)[P]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            a[ks] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds_c[buf][r0 * ROW_BYTES + a_off[ks]]));
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-            acc[p] = ninit;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int p = 0; p < P; ++p)
                 acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), acc[p], 0, 0, 0);
+                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), ks == 0 ? ninit : acc[p], 0, 0, 0);
+            a[ks] = read_a(next_c, next_r0, ks);
+            if (ks == 0)
+                ninit = read_n(next_n, next_r0);
+        }
     };
 
     float bs[P];
@@ -303,32 +336,47 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     };
 
     const int nblocks = (k_rows + BK - 1) / BK;
-    fetch(0);
-    store(0);
+    dma(0, c_st0);
+    load_norm(0);
+    write_norm(n_st0);
+    if (nblocks > 1) {
+        dma(1, c_st1);
+        load_norm(1);
+    }
     __syncthreads();
-    if (nblocks > 1)
-        fetch(1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        a[ks] = read_a(c_st0, 0, ks);
+    ninit = read_n(n_st0, 0);
 
-    f32x16 acc0[P], acc1[P];
-    tile_mfma(0, 0, acc0);
-    for (int b = 0; b < nblocks; ++b) {
-        const int buf = b & 1;
+    // Block b lives in stage cc/nc, block b+1 in cn/nn; block b+2 is fetched
+    // into cc/nc once the barrier shows nobody reads block b any more.
+    auto do_block = [&](int b, uint8_t *cc, float *nc, uint8_t *cn, float *nn) {
         const int kb = k_begin + b * BK;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
-            f32x16(&cur)[P] = (j & 1) ? acc1 : acc0;
-            f32x16(&nxt)[P] = (j & 1) ? acc0 : acc1;
+            f32x16 acc[P];
             if (j + 1 < TB) {
-                tile_mfma(buf, (j + 1) * kTileRows, nxt);
-            } else if (b + 1 < nblocks) {
-                store(buf ^ 1);
-                __syncthreads();
-                if (b + 2 < nblocks)
-                    fetch(b + 2);
-                tile_mfma(buf ^ 1, 0, nxt);
+                compute(cc, nc, (j + 1) * kTileRows, acc);
+            } else {
+                if (b + 1 < nblocks) {
+                    write_norm(nn);
+                    __syncthreads();          // block b+1 is in LDS for every wave
+                    if (b + 2 < nblocks) {
+                        dma(b + 2, cc);
+                        load_norm(b + 2);
+                    }
+                }
+                compute(cn, nn, 0, acc);
             }
-            epilogue(cur, kb + j * kTileRows);
+            epilogue(acc, kb + j * kTileRows);
         }
+    };
+    for (int b = 0; b < nblocks; b += 2) {
+        do_block(b, c_st0, n_st0, c_st1, n_st1);
+        if (b + 1 >= nblocks)
+            break;
+        do_block(b + 1, c_st1, n_st1, c_st0, n_st0);
     }
 
     // ---- merge the two lanes that hold the same point ----

@@ -58,6 +58,56 @@ def traffic_record(config: int):
     return rec
 
 
+def _counter_per_dispatch(csv_path: str, counter: str):
+    """Mean per-dispatch value of `counter` for the assign kernel and for the
+    calibration copy kernel, from a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+    import collections
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            kind = "assign" if "assign_kernel" in name else (
+                "merge" if "merge_kernel" in name else (
+                    "copy" if "neg_kernel" in name else None))
+            if kind is None:
+                continue
+            tot[kind] += float(row["Counter_Value"])
+            disp[kind].add(row["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def record_traffic(config: int, fetch_csv: str, write_csv: str, copy_mib: int, command: str):
+    """Write the HBM-traffic record bench.py reports: counter KiB per assign
+    launch, scaled by what the same counter reads for a plain copy of known
+    size (copy_mib MiB read and written)."""
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
+    known = copy_mib * 1024.0                       # KiB read, and written, by the copy
+    f_scale = known / fetch["copy"]
+    w_scale = known / write["copy"]
+    kib_assign = fetch["assign"] + fetch.get("merge", 0.0)
+    kib_assign_w = write["assign"] + write.get("merge", 0.0)
+    rec = dict(
+        workload=config,
+        kernel_source_hash=kernel_source_hash(),
+        fetch_kib_per_launch=kib_assign,
+        write_kib_per_launch=kib_assign_w,
+        copy_fetch_kib=fetch["copy"], copy_write_kib=write["copy"], copy_kib=known,
+        fetch_scale=f_scale, write_scale=w_scale,
+        hbm_bytes_per_launch=int(round((kib_assign * f_scale + kib_assign_w * w_scale) * 1024)),
+        command=command,
+    )
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_assign_workload{config}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def cpu_baseline(X, C, target_s: float):
     """Time the oracle on the first points of the workload, growing the
     sample until one run takes about ``target_s`` seconds."""
@@ -86,7 +136,17 @@ def main():
                     help="target wall time of the oracle sample (0 disables)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter scale)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic record from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "run made with --copy-calibration-mib; no GPU work")
+    ap.add_argument("--record-command", default="", help="command stored with the record")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(args.config, args.record_traffic[0], args.record_traffic[1],
+                       args.copy_calibration_mib or 256, args.record_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -154,11 +214,13 @@ def main():
           file=sys.stderr, flush=True)
 
     if args.copy_calibration_mib:
+        # A plain streaming kernel of known traffic (read n bytes, write n
+        # bytes) for scaling the HBM byte counters.
         nbytes = args.copy_calibration_mib << 20
         a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        b.copy_(a)
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: {nbytes} bytes read, {nbytes} bytes written",
               file=sys.stderr, flush=True)

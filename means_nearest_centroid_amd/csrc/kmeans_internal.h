@@ -7,8 +7,7 @@
 
 namespace kmeans {
 
-constexpr int kThreads = 256;        // 4 wave64s per workgroup, one per SIMD
-constexpr int kWavesPerWg = 4;
+constexpr int kThreads = 256;        // norms / merge kernels: 4 wave64s
 constexpr int kTileRows = 32;        // centroid rows per MFMA tile (A operand)
 constexpr int kTileCols = 32;        // points per MFMA tile (B operand)
 constexpr int kMaxSplits = 64;
@@ -19,8 +18,10 @@ constexpr int point_blocks_per_wave(int ks) { return ks <= 4 ? 4 : (ks == 8 ? 2 
 // Centroid rows per LDS block (one of two ring stages): whole 32-row tiles,
 // at most one norm per thread, about 32 KiB of centroid data (64 KiB at
 // D = 512, where one workgroup holds a CU).
-constexpr int k_block_rows(int ks) { return ks <= 4 ? 256 : (ks == 8 ? 128 : 64); }
-constexpr int points_per_wg(int ks) { return kWavesPerWg * point_blocks_per_wave(ks) * kTileCols; }
+constexpr int k_block_rows(int ks) { return ks <= 4 ? 256 : (ks == 8 ? 256 : 64); }
+// Waves per assign workgroup (two per SIMD when 8).
+constexpr int waves_per_wg(int ks) { return ks == 8 ? 8 : 4; }
+constexpr int points_per_wg(int ks) { return waves_per_wg(ks) * point_blocks_per_wave(ks) * kTileCols; }
 
 struct Plan {
     int path;          // 1 direct, 2 split (same numbering as kmeans_path_t)

@@ -178,8 +178,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, KM_LDS void *dst
 //       best = m, best_tile = tile, best_slot = slot
 // m is always one of its inputs, so the winner is exact; a strict '<' keeps
 // the earlier tile on equal scores, and the slot search keeps the lower row.
-template <int KS, int P, int BK, int WPE>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+template <int KS, int P, int BK, int WAVES, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
                    const float *__restrict__ norms, int N, int D, int K, int k_chunk,
@@ -190,9 +190,9 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     constexpr int ROW_BYTES = 16 * S;
     constexpr int TB = BK / kTileRows;         // tiles per block
     constexpr int STAGE_BYTES = BK * ROW_BYTES;
-    constexpr int DMA_PER_WAVE = STAGE_BYTES / (1024 * kWavesPerWg);
-    static_assert(STAGE_BYTES % (1024 * kWavesPerWg) == 0, "block must split into 1 KiB DMAs");
-    static_assert(BK % kTileRows == 0 && BK <= kThreads, "block shape");
+    constexpr int DMA_PER_WAVE = STAGE_BYTES / (1024 * WAVES);
+    static_assert(STAGE_BYTES % (1024 * WAVES) == 0, "block must split into 1 KiB DMAs");
+    static_assert(BK % kTileRows == 0 && BK <= 64 * WAVES, "block shape");
 
     __shared__ __attribute__((aligned(16))) uint8_t c_st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t c_st1[STAGE_BYTES];
@@ -208,8 +208,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     const int split = blockIdx.y;
     const int k_begin = split * k_chunk;
     const int k_rows = min(K, k_begin + k_chunk) - k_begin;
-    const int wg_point0 = blockIdx.x * (kWavesPerWg * P * kTileCols);
-    const int wg_points = min(N - wg_point0, kWavesPerWg * P * kTileCols);
+    const int wg_point0 = blockIdx.x * (WAVES * P * kTileCols);
+    const int wg_points = min(N - wg_point0, WAVES * P * kTileCols);
     const uint32_t row_bytes = static_cast<uint32_t>(D) * 2u;
 
     // ---- resident points: -2x as MFMA B fragments, and ||x||^2 ----
@@ -462,9 +462,10 @@ hipError_t launch_assign_ks(const Plan &pl, const uint16_t *X, const uint16_t *C
                             float *ws_xx, hipStream_t stream) {
     constexpr int P = point_blocks_per_wave(KS);
     constexpr int BK = k_block_rows(KS);
+    constexpr int WAVES = waves_per_wg(KS);
     constexpr int WPE = KS >= 32 ? 1 : 2;
     const int partial = ws_score != nullptr ? 1 : 0;
-    hipLaunchKernelGGL((assign_kernel<KS, P, BK, WPE>), dim3(pl.wgs, pl.splits), dim3(kThreads),
+    hipLaunchKernelGGL((assign_kernel<KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
                        0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, labels, min_dist,
                        ws_score, ws_label, ws_xx);
     return hipGetLastError();

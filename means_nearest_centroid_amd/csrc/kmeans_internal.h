@@ -20,7 +20,7 @@ constexpr int point_blocks_per_wave(int ks) { return ks <= 4 ? 4 : (ks == 8 ? 2 
 // D = 512, where one workgroup holds a CU).
 constexpr int k_block_rows(int ks) { return ks <= 4 ? 256 : (ks == 8 ? 256 : 64); }
 // Waves per assign workgroup (two per SIMD when 8).
-constexpr int waves_per_wg(int ks) { return ks == 8 ? 8 : 4; }
+constexpr int waves_per_wg(int ks) { return (ks == 8 || ks == 16) ? 8 : 4; }
 constexpr int points_per_wg(int ks) { return waves_per_wg(ks) * point_blocks_per_wave(ks) * kTileCols; }
 
 struct Plan {

@@ -108,6 +108,83 @@ def record_traffic(config: int, fetch_csv: str, write_csv: str, copy_mib: int, c
     print(json.dumps(rec))
 
 
+# B200 latencies (ms) of the pages' PR path for the 13 sweep shapes
+# (flashlib PR #22, nightly comparison, "Benchmark results" table): another
+# GPU's numbers, printed beside ours as context only.
+PAGES_B200_PR_MS = {
+    (65536, 64, 512): 0.0441, (65536, 64, 4096): 0.1022, (65536, 64, 16384): 0.2963,
+    (65536, 128, 512): 0.0453, (65536, 128, 4096): 0.1059,
+    (262144, 128, 4096): 0.2844, (262144, 128, 16384): 1.0047, (1048576, 128, 4096): 1.0148,
+    (65536, 256, 512): 0.0587, (65536, 256, 4096): 0.1661,
+    (262144, 256, 4096): 0.4631, (262144, 256, 16384): 1.8615, (1048576, 256, 4096): 1.9458,
+}
+
+
+def run_sweep(args):
+    """The pages' 13-shape benchmark: per shape, three seeded sets resident
+    and rotated, ``args.warmup`` untimed then ``args.steps`` timed
+    ``kmeans_assign`` calls (HIP events on the launch stream), median
+    latency; one JSON line per shape, then a geometric-mean line."""
+    import torch
+    import means_nearest_centroid_amd as km
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    km.load_library()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+    lat_ms, ref_ms = [], []
+    for (N, D, K) in W.SWEEP_SHAPES:
+        print(f"[sweep] N={N} D={D} K={K}: generating", file=sys.stderr, flush=True)
+        sets = []
+        for seed in W.SEEDS:
+            X, C, _ = W.gaussian_mixture(N, D, K, seed)
+            Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev)
+            Cd = torch.from_numpy(C.view(np.int16)).view(torch.bfloat16).to(dev)
+            sets.append((Xd, Cd, km.kmeans_centroid_norms(Cd, stream=stream)))
+            del X, C
+        labels = torch.empty(N, dtype=torch.int32, device=dev)
+        min_dist = torch.empty(N, dtype=torch.float32, device=dev)
+        for i in range(args.warmup):
+            X, C, n = sets[i % 3]
+            km.kmeans_assign(X, C, n, labels, min_dist, stream=stream)
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(args.steps):
+            X, C, n = sets[i % 3]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            km.kmeans_assign(X, C, n, labels, min_dist, stream=stream)
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ts])
+        med = float(np.median(ms))
+        plan = km.kmeans_plan(N, D, K, cus)
+        tflops = 2.0 * N * D * K / (med / 1e3) / 1e12
+        ref = PAGES_B200_PR_MS[(N, D, K)]
+        lat_ms.append(med)
+        ref_ms.append(ref)
+        print(json.dumps({
+            "sweep_shape": {"N": N, "D": D, "K": K},
+            "path": "split" if plan["path"] == km.PATH_SPLIT else "direct",
+            "splits": plan["splits"],
+            "median_ms": round(med, 4), "min_ms": round(float(ms.min()), 4),
+            "p90_ms": round(float(np.percentile(ms, 90)), 4),
+            "points_per_s": N / (med / 1e3),
+            "tflops": round(tflops, 1),
+            "frac_bf16_peak": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+            "pages_b200_pr_ms": ref,
+        }), flush=True)
+        del sets, labels, min_dist
+        torch.cuda.empty_cache()
+    geo = float(np.exp(np.mean(np.log(lat_ms))))
+    geo_ref = float(np.exp(np.mean(np.log(ref_ms))))
+    print(json.dumps({"sweep_geomean_ms": round(geo, 4), "shapes": len(lat_ms),
+                      "pages_b200_pr_geomean_ms": round(geo_ref, 4),
+                      "note": "B200 numbers are another GPU's, context only"}), flush=True)
+
+
 def cpu_baseline(X, C, target_s: float):
     """Time the oracle on the first points of the workload, growing the
     sample until one run takes about ``target_s`` seconds."""
@@ -141,6 +218,9 @@ def main():
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "run made with --copy-calibration-mib; no GPU work")
     ap.add_argument("--record-command", default="", help="command stored with the record")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time kmeans_assign on the pages' 13 shapes instead (one JSON "
+                         "line per shape)")
     args = ap.parse_args()
 
     if args.record_traffic:
@@ -152,6 +232,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        run_sweep(args)
+        return
 
     import torch
     import means_nearest_centroid_amd as km
@@ -174,7 +258,7 @@ def main():
     labels = torch.empty(N, dtype=torch.int32, device=dev)
     min_dist = torch.empty(N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    plan = km.kmeans_plan(N, D, K)
+    plan = km.kmeans_plan(N, D, K, torch.cuda.get_device_properties(dev).multi_processor_count)
 
     def step(i, ev=None):
         X, C = sets[i % len(sets)]

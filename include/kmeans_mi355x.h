@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define KMEANS_ABI_VERSION 1
+#define KMEANS_ABI_VERSION 2
 
 /* Supported feature dimension: 16 <= D <= 512 and D % 16 == 0. */
 #define KMEANS_MIN_D 16
@@ -62,7 +62,7 @@ typedef enum {
 typedef enum {
     KMEANS_PATH_AUTO = 0,    /* shape-based choice (what kmeans_assign does) */
     KMEANS_PATH_DIRECT = 1,  /* one pass: every workgroup scans all K centroids */
-    KMEANS_PATH_SPLIT = 2    /* K split over `splits` ranges + a merge pass */
+    KMEANS_PATH_SPLIT = 2    /* K split over `count` ranges + a merge pass */
 } kmeans_path_t;
 
 /*
@@ -98,35 +98,41 @@ kmeans_status_t kmeans_centroid_norms(const void *C, int64_t K, int64_t D,
  * Small-N / large-K shapes run a K-split path whose stream-ordered scratch
  * (8 bytes per point per split + 4 bytes per point) comes from
  * hipMallocAsync/hipFreeAsync on `stream`; KMEANS_ERR_NO_MEMORY if it fails.
- * Both paths give bitwise-identical outputs.
+ * All paths give bitwise-identical outputs.
  */
 kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms,
                               int64_t N, int64_t D, int64_t K, int32_t *labels,
                               float *min_dist, hipStream_t stream);
 
 /*
- * kmeans_assign with the dispatch forced: `path` as in kmeans_path_t and, for
- * KMEANS_PATH_SPLIT, `splits` K-ranges (0 = automatic count; clamped to the
- * number of centroid blocks).  Same arguments, outputs and errors as
- * kmeans_assign; exists so that the two paths can be compared bit for bit.
+ * kmeans_assign with the dispatch forced: `path` as in kmeans_path_t, and
+ * `count` (0 = automatic; ignored by the direct path):
+ *   KMEANS_PATH_SPLIT       number of K-ranges (clamped to 64 and to the
+ *                           number of centroid blocks)
+ * Same arguments, outputs and errors as kmeans_assign (count < 0 is
+ * KMEANS_ERR_INVALID_ARG); exists so that the paths can be compared bit for
+ * bit and timed against each other (the pages' per-shape path table under
+ * "Performance").
  */
 kmeans_status_t kmeans_assign_path(const void *X, const void *C, const float *norms,
                                    int64_t N, int64_t D, int64_t K, int32_t *labels,
-                                   float *min_dist, int32_t path, int32_t splits,
+                                   float *min_dist, int32_t path, int32_t count,
                                    hipStream_t stream);
 
 /*
- * The launch plan kmeans_assign would use for a shape (host only; makes no
- * HIP call).  Any output pointer may be NULL.
+ * The launch plan kmeans_assign would use for a shape on a GPU with
+ * `compute_units` CUs (<= 0: 256, an MI355X); host only, makes no HIP call.
+ * kmeans_assign itself plans with the current device's CU count.  Any output
+ * pointer may be NULL.
  *   path          KMEANS_PATH_DIRECT or KMEANS_PATH_SPLIT
  *   splits        number of K-ranges (1 on the direct path)
- *   workgroups    point-workgroups per K-range
+ *   workgroups    point-workgroups per K-range (grid x)
  *   points_per_wg points owned by one workgroup
  *   k_block       centroid rows staged in LDS per block
  *   padded_d      D rounded up to the kernel's k-step multiple
  */
-kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t *path,
-                            int32_t *splits, int32_t *workgroups,
+kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_units,
+                            int32_t *path, int32_t *splits, int32_t *workgroups,
                             int32_t *points_per_wg, int32_t *k_block,
                             int32_t *padded_d);
 

@@ -70,7 +70,7 @@ def load_library(path: str = LIBRARY):
     lib.kmeans_assign.restype = ctypes.c_int
     lib.kmeans_assign_path.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp]
     lib.kmeans_assign_path.restype = ctypes.c_int
-    lib.kmeans_plan.argtypes = [i64, i64, i64, i32p, i32p, i32p, i32p, i32p, i32p]
+    lib.kmeans_plan.argtypes = [i64, i64, i64, i32, i32p, i32p, i32p, i32p, i32p, i32p]
     lib.kmeans_plan.restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
     lib.kmeans_last_error.restype = ctypes.c_char_p
@@ -111,11 +111,12 @@ def abi_version() -> int:
     return load_library().kmeans_abi_version()
 
 
-def kmeans_plan(N: int, D: int, K: int) -> dict:
-    """Launch plan the library would use for a shape (no GPU needed)."""
+def kmeans_plan(N: int, D: int, K: int, compute_units: int = 0) -> dict:
+    """Launch plan the library would use for a shape on a GPU with
+    ``compute_units`` CUs (0: 256, an MI355X); no GPU needed."""
     lib = load_library()
     vals = [ctypes.c_int32(0) for _ in range(6)]
-    _check(lib, lib.kmeans_plan(N, D, K, *[ctypes.byref(v) for v in vals]))
+    _check(lib, lib.kmeans_plan(N, D, K, compute_units, *[ctypes.byref(v) for v in vals]))
     keys = ("path", "splits", "workgroups", "points_per_wg", "k_block", "padded_d")
     return {k: v.value for k, v in zip(keys, vals)}
 
@@ -159,13 +160,14 @@ def kmeans_assign(X, C, norms, labels=None, min_dist=None, stream=None):
     return labels, min_dist
 
 
-def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, splits: int = 0,
+def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, count: int = 0,
                        labels=None, min_dist=None, stream=None):
-    """``kmeans_assign`` with a forced path (``PATH_DIRECT`` / ``PATH_SPLIT``)."""
+    """``kmeans_assign`` with a forced path (``PATH_DIRECT`` or ``PATH_SPLIT``);
+    ``count`` is the number of K-ranges of the split path (0: automatic)."""
     X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
     lib = load_library()
     _check(lib, lib.kmeans_assign_path(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
-                                       _ptr(min_dist), path, splits, _stream_handle(stream)))
+                                       _ptr(min_dist), path, count, _stream_handle(stream)))
     return labels, min_dist
 
 

@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "kmeans_internal.h"
@@ -31,6 +32,24 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kMaxRows = 0x7fffffffLL - 1024;   // int32 indexing headroom
 
+// Compute units of the current device (cached per device), or the MI355X
+// count when it cannot be queried.
+int device_compute_units() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return kmeans::kDefaultComputeUnits;
+    int cus = cache[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = kmeans::kDefaultComputeUnits;
+        cache[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
 kmeans_status_t check_d(int64_t D) {
     if (D < KMEANS_MIN_D || D > KMEANS_MAX_D || D % 16 != 0)
         return fail(KMEANS_ERR_UNSUPPORTED,
@@ -56,14 +75,14 @@ kmeans_status_t check_shape(int64_t N, int64_t D, int64_t K) {
 
 kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int64_t N,
                            int64_t D, int64_t K, int32_t *labels, float *min_dist,
-                           int path, int splits, hipStream_t stream) {
+                           int path, int count, hipStream_t stream) {
     kmeans_status_t st = check_shape(N, D, K);
     if (st != KMEANS_OK)
         return st;
     if (path < KMEANS_PATH_AUTO || path > KMEANS_PATH_SPLIT)
         return fail(KMEANS_ERR_INVALID_ARG, "path=%d unknown", path);
-    if (splits < 0)
-        return fail(KMEANS_ERR_INVALID_ARG, "splits=%d must be >= 0", splits);
+    if (count < 0)
+        return fail(KMEANS_ERR_INVALID_ARG, "count=%d must be >= 0", count);
     if (N == 0)
         return ok();
     if (!X || !C || !norms || !labels || !min_dist)
@@ -75,7 +94,7 @@ kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int
     if (!aligned(norms, 4) || !aligned(labels, 4) || !aligned(min_dist, 4))
         return fail(KMEANS_ERR_ALIGNMENT, "norms, labels and min_dist must be 4-byte aligned");
 
-    const kmeans::Plan pl = kmeans::make_plan(N, D, K, path, splits);
+    const kmeans::Plan pl = kmeans::make_plan(N, D, K, path, count, device_compute_units());
     const auto *Xb = static_cast<const uint16_t *>(X);
     const auto *Cb = static_cast<const uint16_t *>(C);
     const int n = static_cast<int>(N), d = static_cast<int>(D), k = static_cast<int>(K);
@@ -149,18 +168,19 @@ kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms, 
 
 kmeans_status_t kmeans_assign_path(const void *X, const void *C, const float *norms,
                                    int64_t N, int64_t D, int64_t K, int32_t *labels,
-                                   float *min_dist, int32_t path, int32_t splits,
+                                   float *min_dist, int32_t path, int32_t count,
                                    hipStream_t stream) {
-    return run_assign(X, C, norms, N, D, K, labels, min_dist, path, splits, stream);
+    return run_assign(X, C, norms, N, D, K, labels, min_dist, path, count, stream);
 }
 
-kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t *path, int32_t *splits,
-                            int32_t *workgroups, int32_t *points_per_wg, int32_t *k_block,
-                            int32_t *padded_d) {
+kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_units,
+                            int32_t *path, int32_t *splits, int32_t *workgroups,
+                            int32_t *points_per_wg, int32_t *k_block, int32_t *padded_d) {
     kmeans_status_t st = check_shape(N, D, K);
     if (st != KMEANS_OK)
         return st;
-    const kmeans::Plan pl = kmeans::make_plan(N > 0 ? N : 1, D, K, KMEANS_PATH_AUTO, 0);
+    const kmeans::Plan pl =
+        kmeans::make_plan(N > 0 ? N : 1, D, K, KMEANS_PATH_AUTO, 0, compute_units);
     if (path)
         *path = pl.path;
     if (splits)

@@ -22,20 +22,39 @@ constexpr int k_block_rows(int ks) { return ks <= 4 ? 256 : (ks == 8 ? 256 : 64)
 // Waves per assign workgroup (two per SIMD when 8).
 constexpr int waves_per_wg(int ks) { return (ks == 8 || ks == 16) ? 8 : 4; }
 constexpr int points_per_wg(int ks) { return waves_per_wg(ks) * point_blocks_per_wave(ks) * kTileCols; }
+// Waves per SIMD the kernel's register budget is sized for.
+constexpr int waves_per_simd(int ks) { return ks >= 32 ? 1 : 2; }
+// LDS of one assign workgroup: two centroid stages (BK rows of 32*ks
+// bytes), two norm stages and a 1 KiB cache warm-up line.
+constexpr int assign_lds_bytes(int ks) {
+    return 2 * k_block_rows(ks) * 32 * ks + 2 * k_block_rows(ks) * 4 + 1024;
+}
+constexpr int kLdsPerCu = 160 * 1024;
+// Assign workgroups a CU is guaranteed to hold at once (4 SIMDs; waves and
+// LDS are the limits; registers may allow more at small D).
+constexpr int assign_wgs_per_cu(int ks) {
+    return (4 * waves_per_simd(ks) / waves_per_wg(ks)) < (kLdsPerCu / assign_lds_bytes(ks))
+               ? (4 * waves_per_simd(ks) / waves_per_wg(ks))
+               : (kLdsPerCu / assign_lds_bytes(ks));
+}
+constexpr int kDefaultComputeUnits = 256;   // MI355X
 
 struct Plan {
-    int path;          // 1 direct, 2 split (same numbering as kmeans_path_t)
+    int path;          // 1 direct, 2 split (as kmeans_path_t)
     int splits;        // K-ranges (grid.y)
     int ks;            // padded D / 16
+    int tiles;         // point tiles of ppw points
     int wgs;           // workgroups along N (grid.x)
     int ppw;           // points per workgroup
     int bk;            // centroid rows per LDS block
     int k_chunk;       // centroids per K-range, multiple of bk
 };
 
-// force_path: 0 auto, 1 direct, 2 split; force_splits: 0 auto.
+// force_path: 0 auto, 1 direct, 2 split; force_count: K-ranges (split),
+// 0 auto; compute_units: CUs of the GPU.
 // Requires 1 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller).
-Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_splits);
+Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
+               int compute_units);
 
 hipError_t launch_norms(const uint16_t *C, int K, int D, float *norms, hipStream_t stream);
 

@@ -142,6 +142,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past num_records
 
 #define KM_LDS __attribute__((address_space(3)))
 
+// s_waitcnt vmcnt(0): every vector-memory load this wave issued, LDS DMAs
+// included, has landed.  A workgroup barrier does not imply it on CDNA, and
+// the compiler only adds it where this wave itself reads the data.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
 // lds): lane i writes dst + 16*i.  The builtin exists only for the device
 // target; clang's host pass (which emits the launch stubs and never runs
@@ -343,6 +348,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         dma(1, c_st1);
         load_norm(1);
     }
+    wait_vmem();
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -361,7 +367,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
             } else {
                 if (b + 1 < nblocks) {
                     write_norm(nn);
-                    __syncthreads();          // block b+1 is in LDS for every wave
+                    wait_vmem();              // this wave's DMA of block b+1 ...
+                    __syncthreads();          // ... and everybody else's
                     if (b + 2 < nblocks) {
                         dma(b + 2, cc);
                         load_norm(b + 2);
@@ -463,7 +470,8 @@ hipError_t launch_assign_ks(const Plan &pl, const uint16_t *X, const uint16_t *C
     constexpr int P = point_blocks_per_wave(KS);
     constexpr int BK = k_block_rows(KS);
     constexpr int WAVES = waves_per_wg(KS);
-    constexpr int WPE = KS >= 32 ? 1 : 2;
+    constexpr int WPE = waves_per_simd(KS);
+    static_assert(assign_wgs_per_cu(KS) >= 1, "workgroup must fit a CU");
     const int partial = ws_score != nullptr ? 1 : 0;
     hipLaunchKernelGGL((assign_kernel<KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
                        0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, labels, min_dist,
@@ -504,7 +512,8 @@ hipError_t launch_merge(const Plan &pl, const uint16_t *X, const uint16_t *C,
     return hipGetLastError();
 }
 
-Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_splits) {
+Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
+               int compute_units) {
     Plan pl{};
     int ks_needed = static_cast<int>((D + 15) / 16);
     int ks = 1;
@@ -513,21 +522,28 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_splits
     pl.ks = ks;
     pl.ppw = points_per_wg(ks);
     pl.bk = k_block_rows(ks);
-    pl.wgs = static_cast<int>((N + pl.ppw - 1) / pl.ppw);
+    pl.tiles = static_cast<int>((N + pl.ppw - 1) / pl.ppw);
+    pl.wgs = pl.tiles;
     const int nkb = static_cast<int>((K + pl.bk - 1) / pl.bk);   // centroid blocks
+    const int cus = compute_units > 0 ? compute_units : kDefaultComputeUnits;
 
-    // Fewer point-workgroups than CUs: split K too, aiming at about one
-    // workgroup per CU over all splits.  More splits than that cost more
-    // than they gain (each split re-reads X and adds merge traffic; measured
-    // on the large-K / small-D workload: 2 splits 65 us, 4: 76 us, 8: 85 us).
-    constexpr int kTargetWgs = 256;
+    // Too few point tiles to fill the GPU: split K too, aiming at about 3/4
+    // of the workgroups the GPU holds at once, with at least two centroid
+    // blocks per K-range (the merge pass and the extra launch cost ~10 us,
+    // which a one-block range does not earn back).  Measured at N = 65536
+    // (median us): D=64 K=4096: 2 ranges 72, 3: 66, 4: 85; D=64 K=16384:
+    // 2: 187, 3: 166, 4: 171; D=128 K=4096: 2: 76, 3: 92; D=128 K=16384:
+    // 2: 223, 3: 271; K=512 (two blocks): direct 21, split 30-34.
+    const int target_wgs = 3 * cus * assign_wgs_per_cu(ks) / 4;
     int splits = 1;
     if (force_path == 2) {
-        splits = force_splits > 0 ? force_splits : (kTargetWgs + pl.wgs - 1) / pl.wgs;
+        splits = force_count > 0 ? force_count : (target_wgs + pl.tiles - 1) / pl.tiles;
         if (splits < 1)
             splits = 1;
-    } else if (force_path == 0 && pl.wgs < kTargetWgs) {
-        splits = (kTargetWgs + pl.wgs - 1) / pl.wgs;
+    } else if (force_path == 0 && pl.tiles < target_wgs) {
+        splits = (target_wgs + pl.tiles - 1) / pl.tiles;
+        if (splits > nkb / 2)
+            splits = nkb / 2 > 1 ? nkb / 2 : 1;
     }
     if (splits > kMaxSplits)
         splits = kMaxSplits;

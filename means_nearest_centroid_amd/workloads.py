@@ -292,6 +292,18 @@ def adversarial(N: int, D: int, K: int, seed: int, n_dyadic_pairs: int = 1024,
     return X, C, meta
 
 
+#: The 13 (N, D, K) shapes of the pages' benchmark (flashlib PR #22,
+#: "Performance" table; the same rows in the nightly comparison's "Benchmark
+#: results"), bf16 Gaussian mixtures with K true centres, seeds ``SEEDS``.
+SWEEP_SHAPES = (
+    (65536, 64, 512), (65536, 64, 4096), (65536, 64, 16384),
+    (65536, 128, 512), (65536, 128, 4096),
+    (262144, 128, 4096), (262144, 128, 16384), (1048576, 128, 4096),
+    (65536, 256, 512), (65536, 256, 4096),
+    (262144, 256, 4096), (262144, 256, 16384), (1048576, 256, 4096),
+)
+
+
 def make_config(i: int, seed: int):
     """Inputs of workload ``i`` (1..5) for ``seed``: ``(X, C, meta)``."""
     cfg = CONFIGS[i]

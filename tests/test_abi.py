@@ -86,7 +86,11 @@ def test_assign_empty_is_noop(lib):
 def test_assign_path_rejects_bad_plan(lib):
     st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 64, 5, FAKE, FAKE, 7, 0, NUL)
     assert st == km.KMEANS_ERR_INVALID_ARG
+    st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 64, 5, FAKE, FAKE, 4, 0, NUL)
+    assert st == km.KMEANS_ERR_INVALID_ARG
     st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 64, 5, FAKE, FAKE, 2, -1, NUL)
+    assert st == km.KMEANS_ERR_INVALID_ARG
+    st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 64, 5, FAKE, FAKE, 3, -1, NUL)
     assert st == km.KMEANS_ERR_INVALID_ARG
 
 
@@ -111,6 +115,33 @@ def test_plan_for_the_workloads(lib):
         assert p["padded_d"] >= c["D"] and p["padded_d"] % 16 == 0
         assert p["workgroups"] * p["points_per_wg"] >= c["N"]
         assert p["splits"] * p["k_block"] >= 1
+
+
+# Dispatch on the pages' 13 shapes for a 256-CU GPU (measured choices: the
+# split path only where the point tiles leave the GPU part idle and every
+# K-range keeps at least two centroid blocks).
+SWEEP_PLANS = {
+    (65536, 64, 512): (1, 1), (65536, 64, 4096): (2, 3), (65536, 64, 16384): (2, 3),
+    (65536, 128, 512): (1, 1), (65536, 128, 4096): (2, 2), (262144, 128, 4096): (1, 1),
+    (262144, 128, 16384): (1, 1), (1048576, 128, 4096): (1, 1), (65536, 256, 512): (1, 1),
+    (65536, 256, 4096): (1, 1), (262144, 256, 4096): (1, 1), (262144, 256, 16384): (1, 1),
+    (1048576, 256, 4096): (1, 1),
+}
+
+
+def test_plan_for_the_sweep_shapes(lib):
+    from means_nearest_centroid_amd.workloads import SWEEP_SHAPES
+    assert set(SWEEP_SHAPES) == set(SWEEP_PLANS)
+    for shape, (path, splits) in SWEEP_PLANS.items():
+        p = km.kmeans_plan(*shape, 256)
+        assert (p["path"], p["splits"]) == (path, splits), shape
+        assert km.kmeans_plan(*shape) == p      # 0 CUs: the MI355X default
+
+
+def test_plan_follows_the_compute_unit_count(lib):
+    assert km.kmeans_plan(65536, 128, 4096, 256)["path"] == km.PATH_SPLIT
+    assert km.kmeans_plan(65536, 128, 4096, 128)["path"] == km.PATH_DIRECT
+    assert km.kmeans_plan(65536, 128, 4096, 1024)["splits"] == 6
 
 
 @pytest.mark.parametrize("N,D,K", [(1, 16, 1), (100, 80, 7), (5000, 192, 3000),

@@ -33,10 +33,10 @@ def dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def run(X, C, path=km.PATH_AUTO, splits=0):
+def run(X, C, path=km.PATH_AUTO, count=0):
     Xd, Cd = dev(X), dev(C)
     n = km.kmeans_centroid_norms(Cd)
-    lab, md = km.kmeans_assign_path(Xd, Cd, n, path, splits)
+    lab, md = km.kmeans_assign_path(Xd, Cd, n, path, count)
     torch.cuda.synchronize()
     return lab.cpu().numpy(), md.cpu().numpy()
 
@@ -69,12 +69,13 @@ SMALL = [  # (N, D, K): ragged tails in every dimension, several tiles
 ]
 
 
-@pytest.mark.parametrize("path", [km.PATH_AUTO, km.PATH_DIRECT, km.PATH_SPLIT],
-                         ids=["auto", "direct", "split"])
+@pytest.mark.parametrize("path,count", [(km.PATH_AUTO, 0), (km.PATH_DIRECT, 0),
+                                        (km.PATH_SPLIT, 0), (km.PATH_SPLIT, 3)],
+                         ids=["auto", "direct", "split", "split3"])
 @pytest.mark.parametrize("N,D,K", SMALL)
-def test_small_shapes(N, D, K, path):
+def test_small_shapes(N, D, K, path, count):
     X, C, _ = W.gaussian_mixture(N, D, K, 1000 + N + K)
-    lab, md = run(X, C, path)
+    lab, md = run(X, C, path, count)
     parity.check(X, C, lab, md)
 
 
@@ -110,6 +111,21 @@ def test_workload4_sampled():
     X, C, _ = W.make_config(4, 17)
     lab, md = run(X, C)
     parity.check(X, C, lab, md, idx=parity.sample_indices(X.shape[0], 4, 1024, 1024))
+
+
+# The pages' 13 benchmark shapes.  The pages checked the first 2048
+# assignments of every seeded set; here those plus random and tail samples
+# (all three seeds up to N = 262144, seed 17 at N = 1048576).
+SWEEP_CASES = [(n, d, k, seed) for (n, d, k) in W.SWEEP_SHAPES
+               for seed in (W.SEEDS if n <= 262144 else W.SEEDS[:1])]
+
+
+@pytest.mark.parametrize("N,D,K,seed", SWEEP_CASES,
+                         ids=[f"{n}x{d}x{k}-s{s}" for n, d, k, s in SWEEP_CASES])
+def test_sweep_shape_sampled(N, D, K, seed):
+    X, C, _ = W.gaussian_mixture(N, D, K, seed)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md, idx=parity.sample_indices(N, seed, 2048, 512, 64))
 
 
 @pytest.fixture(scope="module")
@@ -163,8 +179,8 @@ def test_nonfinite_centroids():
     X[10, 3] = W.BF16_PINF
     X[11, 4] = W.BF16_NINF
     X[12, 5] = W.BF16_QNAN
-    for path in (km.PATH_DIRECT, km.PATH_SPLIT):
-        lab, md = run(X, C, path)
+    for path, count in ((km.PATH_DIRECT, 0), (km.PATH_SPLIT, 0), (km.PATH_SPLIT, 3)):
+        lab, md = run(X, C, path, count)
         parity.check(X, C, lab, md)
 
 

@@ -10,8 +10,11 @@ rotating seeded bf16 sets, warmup calls, then timed calls).
 Prints one JSON line.  ``value`` = points assigned per second over the timed
 steps (GPU-event time, inputs already on the device).  ``roofline`` reports
 the assign kernel against the bf16 dense MFMA peak, with its average launch
-duration measured by HIP events on the launch stream.  ``cpu_baseline`` times
-the CPU oracle on a bounded sample of the same workload.
+duration measured by HIP events on the launch stream.  ``mfma_ceiling`` is
+the rate of the same MFMA issued back to back on this workload's operand
+values (no memory, no epilogue): what the matrix pipe sustains on this data,
+against which ``roofline.achieved`` is also read.  ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -185,6 +188,56 @@ def run_sweep(args):
                       "note": "B200 numbers are another GPU's, context only"}), flush=True)
 
 
+def mfma_ceiling(X, C, dev, cus: int, tiles: int = 2000, reps: int = 3):
+    """Rate of the MFMA-only probe (libkmeans_mfma_stream.so) on operand rows
+    made of this workload's values (points scaled by -2, as the assign kernel
+    holds them, and centroids), and on zero operands: the matrix pipe's
+    ceiling for this data on this GPU."""
+    import ctypes
+    import torch
+    from means_nearest_centroid_amd import build as kbuild
+    lib = ctypes.CDLL(kbuild.PROBE_LIBRARY)
+    lib.kmeans_mfma_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.kmeans_mfma_stream.restype = ctypes.c_int32
+    threads = lib.kmeans_mfma_stream_threads()
+    rows = int(min(8192, X.size // 128, C.size // 128))
+
+    def operand(bits, scale):
+        v = torch.from_numpy(bits.reshape(-1)[:rows * 128].view(np.int16)).view(torch.bfloat16)
+        return (v.to(dev).float() * scale).to(torch.bfloat16).reshape(rows, 128).contiguous()
+
+    wgs = 2 * cus
+    sink = torch.empty(wgs * threads, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    flop = 2.0 * 32 * 32 * 16 * 16 * tiles * wgs * (threads // 64)
+
+    def rate(a, b):
+        ts = []
+        for r in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = lib.kmeans_mfma_stream(a.data_ptr(), b.data_ptr(), rows, tiles, wgs,
+                                        sink.data_ptr(), stream.cuda_stream)
+            e1.record(stream)
+            if st != 0:
+                raise RuntimeError(f"kmeans_mfma_stream failed ({st})")
+            e1.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        return flop / float(np.median(ts)) / 1e12
+
+    data = rate(operand(C, 1.0), operand(X, -2.0))
+    z = torch.zeros((rows, 128), dtype=torch.bfloat16, device=dev)
+    zero = rate(z, z)
+    return dict(probe="kmeans_mfma_stream: the assign kernel's MFMA back to back, no LDS, "
+                      "no epilogue; operands = this workload's rows (x scaled by -2, centroids)",
+                tflops=round(data, 1), frac_of_peak=round(data / BF16_DENSE_PEAK_TFLOPS, 4),
+                zero_operand_tflops=round(zero, 1))
+
+
 def cpu_baseline(X, C, target_s: float):
     """Time the oracle on the first points of the workload, growing the
     sample until one run takes about ``target_s`` seconds."""
@@ -218,6 +271,8 @@ def main():
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "run made with --copy-calibration-mib; no GPU work")
     ap.add_argument("--record-command", default="", help="command stored with the record")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the MFMA-only probe (mfma_ceiling: null)")
     ap.add_argument("--sweep", action="store_true",
                     help="time kmeans_assign on the pages' 13 shapes instead (one JSON "
                          "line per shape)")
@@ -321,6 +376,13 @@ def main():
                     avg_launch_us=round(avg_assign_s * 1e6, 2),
                     flop_per_launch=flops)
 
+    ceiling = None
+    if not args.no_ceiling:
+        print("[bench] MFMA-only probe on this workload's operands", file=sys.stderr, flush=True)
+        X0, C0 = host_sets[0]
+        ceiling = mfma_ceiling(X0, C0, dev, torch.cuda.get_device_properties(dev).multi_processor_count)
+        ceiling["assign_frac_of_ceiling"] = round(achieved / ceiling["tflops"], 4)
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -348,6 +410,7 @@ def main():
             "splits": plan["splits"],
         },
         "roofline": roofline,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "breakdown_us": {
             "norms_median": round(float(np.median(norms_ms)) * 1e3, 2),

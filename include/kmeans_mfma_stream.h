@@ -1,0 +1,50 @@
+/*
+ * kmeans_mfma_stream.h -- measurement probe shipped beside the assignment
+ * library (libkmeans_mfma_stream.so); not part of the assignment path.
+ *
+ * A back-to-back stream of the assign kernel's MFMA (bf16 x bf16 -> fp32,
+ * 32x32x16) on operands the caller supplies, with no memory traffic or
+ * epilogue in the loop.  Its flop rate is the ceiling of the matrix pipe for
+ * those bit patterns on the running GPU (the part lowers its clock under
+ * dense bf16 MFMA with realistic data), against which the assign kernel's
+ * rate can be read.
+ */
+#ifndef KMEANS_MFMA_STREAM_H
+#define KMEANS_MFMA_STREAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Launch `workgroups` workgroups of kmeans_mfma_stream_threads() threads
+ * (4 waves, 2 waves per SIMD); each wave issues 16 * (1 + 2 * floor(tiles / 2))
+ * MFMAs of 32*32*16*2 flop (16 * tiles for odd `tiles`).  Asynchronous on `stream`; time it with events.
+ *
+ *   a_rows, b_rows  bf16 [rows][128], device, 16-byte aligned: the A
+ *                   (centroid-like) and B (point-like) operand rows; wave w
+ *                   uses A rows 32w.. and B rows 64w.. modulo `rows`.
+ *   rows            >= 1
+ *   tiles           >= 1
+ *   workgroups      1..65536 (two per CU fill the GPU at 2 waves per SIMD)
+ *   sink            fp32 [workgroups * kmeans_mfma_stream_threads()], device,
+ *                   written (keeps the results alive).
+ *
+ * Returns 0, 1 for an invalid argument (nothing launched), 2 if the launch
+ * failed.
+ */
+int32_t kmeans_mfma_stream(const void *a_rows, const void *b_rows, int32_t rows,
+                           int32_t tiles, int32_t workgroups, float *sink,
+                           hipStream_t stream);
+
+/* Threads per workgroup of kmeans_mfma_stream. */
+int32_t kmeans_mfma_stream_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KMEANS_MFMA_STREAM_H */

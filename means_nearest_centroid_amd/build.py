@@ -1,4 +1,6 @@
-"""Build the HIP library ``libkmeans_mi355x.so`` in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950: ``libkmeans_mi355x.so`` (the
+assignment path) and ``libkmeans_mfma_stream.so`` (the MFMA-rate probe that
+bench.py reads the assign kernel's rate against).
 
 Run as ``python -m means_nearest_centroid_amd.build``.  hipcc cross-compiles
 without a GPU present.
@@ -17,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libkmeans_mi355x.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("kmeans_kernels.hip", "kmeans_api.hip")]
+PROBE_LIBRARY = os.path.join(PKG, "libkmeans_mfma_stream.so")
+PROBE_SOURCES = [os.path.join(CSRC, "mfma_stream.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are switched off for all device code.
@@ -34,9 +38,9 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+def _compile(sources, output, verbose, extra_flags):
+    tmp = output + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,8 +50,14 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, output)
+    return output
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile both libraries; returns the assignment library's path."""
+    _compile(PROBE_SOURCES, PROBE_LIBRARY, verbose, extra_flags)
+    return _compile(SOURCES, LIBRARY, verbose, extra_flags)
 
 
 if __name__ == "__main__":

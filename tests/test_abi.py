@@ -38,6 +38,27 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), f"{name} declared in the header but not exported"
 
 
+def test_probe_library_exports_its_header():
+    from means_nearest_centroid_amd import build as kbuild
+    if not os.path.exists(kbuild.PROBE_LIBRARY):
+        kbuild.build()
+    probe = ctypes.CDLL(kbuild.PROBE_LIBRARY)
+    header = os.path.join(os.path.dirname(km.HEADER), "kmeans_mfma_stream.h")
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(kmeans_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["kmeans_mfma_stream", "kmeans_mfma_stream_threads"]
+    for name in names:
+        assert hasattr(probe, name)
+    assert probe.kmeans_mfma_stream_threads() == 256
+    f = probe.kmeans_mfma_stream
+    f.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 2
+    # invalid arguments are refused before any HIP call
+    assert f(None, FAKE, 64, 10, 1, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, 0, 10, 1, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, 64, 10, 70000, FAKE, NUL) == 1
+    assert f(FAKE_ODD, FAKE, 64, 10, 1, FAKE, NUL) == 1
+
+
 def test_abi_version(lib):
     m = re.search(r"#define\s+KMEANS_ABI_VERSION\s+(\d+)", open(km.HEADER).read())
     assert lib.kmeans_abi_version() == int(m.group(1))

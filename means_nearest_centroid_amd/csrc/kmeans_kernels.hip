@@ -19,8 +19,9 @@
 //    double-buffered through LDS with an XOR swizzle so the A-operand reads
 //    (ds_read_b128, 32 rows at one column) hit distinct banks.  Buffer loads
 //    return zero past the end, so ragged N, K and D need no branches.
-//  * Accumulators are double-buffered so the MFMAs of the next tile are in
-//    flight while the VALU reduces the current one.
+//  * Reductions never wait on the matrix pipe: a point block's scores are
+//    reduced only after the MFMAs of the next point block (or tile) have
+//    been issued, so the VALU work runs while those MFMAs execute.
 //  * The epilogue does not run one compare-select chain per score (the
 //    pages' serial scan and its "Two-chain argmin" ILP fix): on CDNA4 an
 //    index can only enter a v_cndmask as a VGPR or an inline constant, so a
@@ -141,6 +142,10 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past num_records
 
 #define KM_LDS __attribute__((address_space(3)))
+// The assign kernel's lambdas must be inlined before its arrays (resident
+// points, fragments, accumulators) are promoted to registers; left to the
+// inliner, a late inline can leave such an array in scratch memory.
+#define KM_INLINE __attribute__((always_inline))
 
 // s_waitcnt vmcnt(0): every vector-memory load this wave issued, LDS DMAs
 // included, has landed.  A workgroup barrier does not imply it on CDNA, and
@@ -248,7 +253,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         const int r = o / ROW_BYTES, c = swz<S>(r, (o % ROW_BYTES) / 16);
         dma_src[i] = c * 8 < D ? static_cast<uint32_t>(r) * row_bytes + c * 16 : kOutOfRange;
     }
-    auto dma = [&](int blk, uint8_t *stage) {
+    auto dma = [&](int blk, uint8_t *stage) KM_INLINE {
         const uint32_t base = static_cast<uint32_t>(blk) * BK * row_bytes;
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i)
@@ -257,7 +262,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     };
     uint32_t nbits = 0;
     bool nvalid = false;
-    auto load_norm = [&](int blk) {
+    auto load_norm = [&](int blk) KM_INLINE {
         if (tid < BK) {
             const int r = blk * BK + tid;
             nbits = static_cast<uint32_t>(
@@ -265,7 +270,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
             nvalid = r < k_rows;
         }
     };
-    auto write_norm = [&](float *stage) {
+    auto write_norm = [&](float *stage) KM_INLINE {
         // Rows past the range score NaN, which never wins.
         if (tid < BK)
             stage[tid] = nvalid ? __uint_as_float(nbits) : __builtin_nanf("");
@@ -277,13 +282,13 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         a_off[ks] = col * ROW_BYTES + swz<S>(col, 2 * ks + half) * 16;
-    auto read_a = [&](const uint8_t *stage, int r0, int ks) {
+    auto read_a = [&](const uint8_t *stage, int r0, int ks) KM_INLINE {
         return __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4 *>(&stage[r0 * ROW_BYTES + a_off[ks]]));
     };
     // Norm tile as the MFMA C input: slot r of this lane is tile row
     // 8*(r/4) + 4*half + r%4.
-    auto read_n = [&](const float *stage, int r0) {
+    auto read_n = [&](const float *stage, int r0) KM_INLINE {
         f32x16 v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -297,20 +302,6 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 
     bf16x8 a[KS];
     f32x16 ninit;
-    // MFMAs of the current tile (operands a, ninit); each operand register is
-    // refilled with the next tile's fragment right after its last use.
-    auto compute = [&](const uint8_t *next_c, const float *next_n, int next_r0, f32x16 (&acc)[P]) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), ks == 0 ? ninit : acc[p], 0, 0, 0);
-            a[ks] = read_a(next_c, next_r0, ks);
-            if (ks == 0)
-                ninit = read_n(next_n, next_r0);
-        }
-    };
 
     float bs[P];
     int32_t bt[P], bo[P];
@@ -320,23 +311,60 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         bt[p] = kNoLabel;
         bo[p] = 0;
     }
-    // acc[p][r] = s for centroid kt + 8*(r/4) + 4*half + r%4.
-    auto epilogue = [&](const f32x16 (&acc)[P], int kt) {
+    // Fold the 16 scores of point block p in v (centroids kt + 8*(r/4) +
+    // 4*half + r%4) into that block's running best.
+    auto reduce = [&](int p, const f32x16 &v, int kt) KM_INLINE {
+        float m = bs[p];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+            m = __builtin_fminf(__builtin_fminf(m, v[r]), v[r + 1]);
+        if (m < bs[p]) {
+            int slot = 0;
+#pragma unroll
+            for (int r = 15; r >= 0; --r)
+                slot = v[r] == m ? 8 * (r >> 2) + (r & 3) : slot;
+            bs[p] = m;
+            bt[p] = kt;
+            bo[p] = slot;
+        }
+    };
+
+    // With several point blocks per wave, every reduction reads MFMA results
+    // issued a whole chain earlier: point block p's MFMAs are issued, then
+    // block p-1 is reduced while they run (the previous tile's last block
+    // after the first block of this tile; its slot holds +inf before the
+    // first tile).  With one point block a tile is reduced right after its
+    // own MFMAs (a second accumulator does not fit the register budget) and
+    // the other wave of the SIMD keeps the matrix pipe busy meanwhile.
+    constexpr bool ROTATE = P > 1;
+    f32x16 acc[P];
+    if (ROTATE) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[P - 1][r] = INFINITY;
+    }
+    // One tile: MFMAs with the current operands (a, ninit), whose registers
+    // are refilled with the next tile's fragments right after their last
+    // use, interleaved with the reductions.
+    auto tile = [&](const uint8_t *next_c, const float *next_n, int next_r0, int kt) KM_INLINE {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            float m = bs[p];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2)
-                m = __builtin_fminf(__builtin_fminf(m, acc[p][r]), acc[p][r + 1]);
-            if (m < bs[p]) {
-                int slot = 0;
-#pragma unroll
-                for (int r = 15; r >= 0; --r)
-                    slot = acc[p][r] == m ? 8 * (r >> 2) + (r & 3) : slot;
-                bs[p] = m;
-                bt[p] = kt;
-                bo[p] = slot;
+            for (int ks = 0; ks < KS; ++ks) {
+                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), ks == 0 ? ninit : acc[p], 0, 0, 0);
+                if (p == P - 1) {
+                    a[ks] = read_a(next_c, next_r0, ks);
+                    if (ks == 0)
+                        ninit = read_n(next_n, next_r0);
+                }
             }
+            if (!ROTATE)
+                reduce(0, acc[0], kt);
+            else if (p == 0)
+                reduce(P - 1, acc[P - 1], kt - kTileRows);
+            else
+                reduce(p - 1, acc[p - 1], kt);
         }
     };
 
@@ -357,13 +385,12 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 
     // Block b lives in stage cc/nc, block b+1 in cn/nn; block b+2 is fetched
     // into cc/nc once the barrier shows nobody reads block b any more.
-    auto do_block = [&](int b, uint8_t *cc, float *nc, uint8_t *cn, float *nn) {
+    auto do_block = [&](int b, uint8_t *cc, float *nc, uint8_t *cn, float *nn) KM_INLINE {
         const int kb = k_begin + b * BK;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
-            f32x16 acc[P];
             if (j + 1 < TB) {
-                compute(cc, nc, (j + 1) * kTileRows, acc);
+                tile(cc, nc, (j + 1) * kTileRows, kb + j * kTileRows);
             } else {
                 if (b + 1 < nblocks) {
                     write_norm(nn);
@@ -374,9 +401,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                         load_norm(b + 2);
                     }
                 }
-                compute(cn, nn, 0, acc);
+                tile(cn, nn, 0, kb + j * kTileRows);
             }
-            epilogue(acc, kb + j * kTileRows);
         }
     };
     for (int b = 0; b < nblocks; b += 2) {
@@ -385,6 +411,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
             break;
         do_block(b + 1, c_st1, n_st1, c_st0, n_st0);
     }
+    if (ROTATE)   // the last tile's last point block
+        reduce(P - 1, acc[P - 1], k_begin + (nblocks - 1) * BK + (TB - 1) * kTileRows);
 
     // ---- merge the two lanes that hold the same point ----
 #pragma unroll

@@ -222,23 +222,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     const int wg_points = min(N - wg_point0, WAVES * P * kTileCols);
     const uint32_t row_bytes = static_cast<uint32_t>(D) * 2u;
 
-    // ---- resident points: -2x as MFMA B fragments, and ||x||^2 ----
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + static_cast<size_t>(wg_point0) * D,
-                                                static_cast<uint32_t>(wg_points) * row_bytes);
-    u32x4 xb[P][KS];
+    u32x4 xb[P][KS];     // resident points (-2x), loaded below
     float xx[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        xx[p] = 0.0f;
-        const uint32_t prow = static_cast<uint32_t>((wave * P + p) * kTileCols + col);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c0 = ks * 16 + half * 8;
-            const uint32_t off = c0 < D ? prow * row_bytes + c0 * 2 : kOutOfRange;
-            xb[p][ks] = neg2_and_square(load16(xr, off), xx[p]);
-        }
-        xx[p] += __shfl_xor(xx[p], 32);
-    }
 
     // ---- centroid blocks: DMA into the LDS ring, norms via one register ----
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(C + static_cast<size_t>(k_begin) * D,
@@ -371,13 +356,41 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     const int nblocks = (k_rows + BK - 1) / BK;
     dma(0, c_st0);
     load_norm(0);
+
+    // ---- resident points: -2x as MFMA B fragments, and ||x||^2 ----
+    // Loaded after block 0's DMA is issued, so that the conversion below,
+    // which waits for the points, does not hold the DMA back.
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + static_cast<size_t>(wg_point0) * D,
+                                                static_cast<uint32_t>(wg_points) * row_bytes);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint32_t prow = static_cast<uint32_t>((wave * P + p) * kTileCols + col);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c0 = ks * 16 + half * 8;
+            xb[p][ks] = load16(xr, c0 < D ? prow * row_bytes + c0 * 2 : kOutOfRange);
+        }
+    }
+    // Keep the conversion below the loads: pulled up between them, each of its
+    // waits would also wait for block 0's DMA (loads complete in order).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        xx[p] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            xb[p][ks] = neg2_and_square(xb[p][ks], xx[p]);
+        xx[p] += __shfl_xor(xx[p], 32);
+    }
+
+    wait_vmem();      // block 0, its norms and the points, in one round trip
     write_norm(n_st0);
+    __syncthreads();
+    // Block 1 is first read after block 0's barrier, a whole block later.
     if (nblocks > 1) {
         dma(1, c_st1);
         load_norm(1);
     }
-    wait_vmem();
-    __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         a[ks] = read_a(c_st0, 0, ks);

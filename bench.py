@@ -7,8 +7,10 @@ three seeded sets (17, 29, 43) resident in HBM and rotated between steps
 (flashlib PR #22, nightly-comparison section, "Benchmark methodology":
 rotating seeded bf16 sets, warmup calls, then timed calls).
 
-Prints one JSON line.  ``value`` = points assigned per second over the timed
-steps (GPU-event time, inputs already on the device).  ``roofline`` reports
+Before the warmup steps the step runs untimed for ``--settle-ms`` (250 ms):
+the first milliseconds after idle run at lower clocks.  Prints one JSON line.
+``value`` = points assigned per second over the timed steps (GPU-event time,
+inputs already on the device).  ``roofline`` reports
 the assign kernel against the bf16 dense MFMA peak, with its average launch
 duration measured by HIP events on the launch stream.  ``mfma_ceiling`` is
 the rate of the same MFMA issued back to back on this workload's operand
@@ -125,9 +127,10 @@ PAGES_B200_PR_MS = {
 
 def run_sweep(args):
     """The pages' 13-shape benchmark: per shape, three seeded sets resident
-    and rotated, ``args.warmup`` untimed then ``args.steps`` timed
-    ``kmeans_assign`` calls (HIP events on the launch stream), median
-    latency; one JSON line per shape, then a geometric-mean line."""
+    and rotated, ``args.settle_ms`` of untimed calls, ``args.warmup``
+    untimed then ``args.steps`` timed ``kmeans_assign`` calls (HIP events on
+    the launch stream), median latency; one JSON line per shape, then a
+    geometric-mean line."""
     import torch
     import means_nearest_centroid_amd as km
     dev = torch.device("cuda:0")
@@ -147,9 +150,14 @@ def run_sweep(args):
             del X, C
         labels = torch.empty(N, dtype=torch.int32, device=dev)
         min_dist = torch.empty(N, dtype=torch.float32, device=dev)
-        for i in range(args.warmup):
+
+        def call(i):
             X, C, n = sets[i % 3]
             km.kmeans_assign(X, C, n, labels, min_dist, stream=stream)
+
+        settle(call, args.settle_ms)
+        for i in range(args.warmup):
+            call(i)
         torch.cuda.synchronize()
         ts = []
         for i in range(args.steps):
@@ -186,6 +194,24 @@ def run_sweep(args):
     print(json.dumps({"sweep_geomean_ms": round(geo, 4), "shapes": len(lat_ms),
                       "pages_b200_pr_geomean_ms": round(geo_ref, 4),
                       "note": "B200 numbers are another GPU's, context only"}), flush=True)
+
+
+def settle(step, ms: float):
+    """Run ``step(i)`` untimed until ``ms`` of wall time have passed: a GPU
+    coming out of idle runs its first milliseconds of dense MFMA work at
+    lower clocks (10 warmup steps of the headline workload are ~3 ms and
+    measured ~15% slower than steady state).  Returns the steps run."""
+    import torch
+    if ms <= 0:
+        return 0
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def mfma_ceiling(X, C, dev, cus: int, tiles: int = 2000, reps: int = 3):
@@ -262,6 +288,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=sorted(W.CONFIGS))
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="untimed steps for this long before the warmup steps, so the "
+                         "timed steps run at steady-state clocks (0 disables)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample (0 disables)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -327,7 +356,9 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    settled = settle(step, args.settle_ms)
+    print(f"[bench] settled clocks with {settled} untimed steps; warmup {args.warmup} steps",
+          file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -407,7 +438,7 @@ def main():
             "workload": f"kmeans assignment, {cfg['name']}, bf16 Gaussian mixture, "
                         f"seeds {list(W.SEEDS)} rotated",
             "N": N, "D": D, "K": K, "path": "split" if plan["path"] == 2 else "direct",
-            "splits": plan["splits"],
+            "splits": plan["splits"], "settle_ms": args.settle_ms, "settle_steps": settled,
         },
         "roofline": roofline,
         "mfma_ceiling": ceiling,

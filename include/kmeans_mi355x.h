@@ -106,9 +106,13 @@ kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms,
 
 /*
  * kmeans_assign with the dispatch forced: `path` as in kmeans_path_t, and
- * `count` (0 = automatic; ignored by the direct path):
+ * `count` (0 = automatic):
+ *   KMEANS_PATH_DIRECT      1: narrow point tiles (32 points per wave), any
+ *                           other value: wide tiles (as many points per wave
+ *                           as the registers hold; the automatic choice for
+ *                           large N)
  *   KMEANS_PATH_SPLIT       number of K-ranges (clamped to 64 and to the
- *                           number of centroid blocks)
+ *                           number of centroid blocks), wide tiles
  * Same arguments, outputs and errors as kmeans_assign (count < 0 is
  * KMEANS_ERR_INVALID_ARG); exists so that the paths can be compared bit for
  * bit and timed against each other (the pages' per-shape path table under

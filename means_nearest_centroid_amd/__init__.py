@@ -162,8 +162,10 @@ def kmeans_assign(X, C, norms, labels=None, min_dist=None, stream=None):
 
 def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, count: int = 0,
                        labels=None, min_dist=None, stream=None):
-    """``kmeans_assign`` with a forced path (``PATH_DIRECT`` or ``PATH_SPLIT``);
-    ``count`` is the number of K-ranges of the split path (0: automatic)."""
+    """``kmeans_assign`` with a forced path (``PATH_DIRECT`` or ``PATH_SPLIT``).
+    ``count``: for the split path the number of K-ranges (0: automatic); for
+    the direct path 1 selects narrow point tiles (32 points per wave), any
+    other value wide ones."""
     X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
     lib = load_library()
     _check(lib, lib.kmeans_assign_path(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),

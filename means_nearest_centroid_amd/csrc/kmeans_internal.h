@@ -14,14 +14,18 @@ constexpr int kMaxSplits = 64;
 constexpr int32_t kNoLabel = 0x7fffffff;
 
 // Kernel shape for a padded feature width of 16*ks (ks a power of two).
-constexpr int point_blocks_per_wave(int ks) { return ks <= 4 ? 4 : (ks == 8 ? 2 : 1); }
+// Point blocks (32 points each) per wave of a wide tile: as many as the
+// register budget holds, so each centroid fragment read from LDS feeds that
+// many MFMAs.  Narrow tiles (one block per wave) trade that reuse for four
+// (D <= 64) or two (D = 128) times as many workgroups when N is small.
+constexpr int wide_point_blocks(int ks) { return ks <= 4 ? 4 : (ks == 8 ? 2 : 1); }
 // Centroid rows per LDS block (one of two ring stages): whole 32-row tiles,
 // at most one norm per thread, about 32 KiB of centroid data (64 KiB at
 // D = 512, where one workgroup holds a CU).
 constexpr int k_block_rows(int ks) { return ks <= 4 ? 256 : (ks == 8 ? 256 : 64); }
 // Waves per assign workgroup (two per SIMD when 8).
 constexpr int waves_per_wg(int ks) { return (ks == 8 || ks == 16) ? 8 : 4; }
-constexpr int points_per_wg(int ks) { return waves_per_wg(ks) * point_blocks_per_wave(ks) * kTileCols; }
+constexpr int points_per_wg(int ks, int pb) { return waves_per_wg(ks) * pb * kTileCols; }
 // Waves per SIMD the kernel's register budget is sized for.
 constexpr int waves_per_simd(int ks) { return ks >= 32 ? 1 : 2; }
 // LDS of one assign workgroup: two centroid stages (BK rows of 32*ks
@@ -43,6 +47,7 @@ struct Plan {
     int path;          // 1 direct, 2 split (as kmeans_path_t)
     int splits;        // K-ranges (grid.y)
     int ks;            // padded D / 16
+    int pb;            // point blocks per wave (wide_point_blocks(ks) or 1)
     int tiles;         // point tiles of ppw points
     int wgs;           // workgroups along N (grid.x)
     int ppw;           // points per workgroup
@@ -50,8 +55,9 @@ struct Plan {
     int k_chunk;       // centroids per K-range, multiple of bk
 };
 
-// force_path: 0 auto, 1 direct, 2 split; force_count: K-ranges (split),
-// 0 auto; compute_units: CUs of the GPU.
+// force_path: 0 auto, 1 direct, 2 split; force_count: K-ranges (split) or
+// point blocks per wave (direct: 1 narrow, other wide), 0 auto;
+// compute_units: CUs of the GPU.
 // Requires 1 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller).
 Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
                int compute_units);

@@ -503,12 +503,11 @@ void norms_kernel(const uint16_t *__restrict__ C, int K, int D, float *__restric
         norms[row] = acc;
 }
 
-template <int KS>
-hipError_t launch_assign_ks(const Plan &pl, const uint16_t *X, const uint16_t *C,
+template <int KS, int P>
+hipError_t launch_assign_kp(const Plan &pl, const uint16_t *X, const uint16_t *C,
                             const float *norms, int N, int D, int K, int32_t *labels,
                             float *min_dist, float *ws_score, int32_t *ws_label,
                             float *ws_xx, hipStream_t stream) {
-    constexpr int P = point_blocks_per_wave(KS);
     constexpr int BK = k_block_rows(KS);
     constexpr int WAVES = waves_per_wg(KS);
     constexpr int WPE = waves_per_simd(KS);
@@ -518,6 +517,19 @@ hipError_t launch_assign_ks(const Plan &pl, const uint16_t *X, const uint16_t *C
                        0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, labels, min_dist,
                        ws_score, ws_label, ws_xx);
     return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_assign_ks(const Plan &pl, const uint16_t *X, const uint16_t *C,
+                            const float *norms, int N, int D, int K, int32_t *labels,
+                            float *min_dist, float *ws_score, int32_t *ws_label,
+                            float *ws_xx, hipStream_t stream) {
+    constexpr int WIDE = wide_point_blocks(KS);
+    if (WIDE > 1 && pl.pb == 1)
+        return launch_assign_kp<KS, 1>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
+                                       ws_label, ws_xx, stream);
+    return launch_assign_kp<KS, WIDE>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
+                                      ws_label, ws_xx, stream);
 }
 
 }  // namespace
@@ -561,27 +573,43 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
     while (ks < ks_needed)
         ks <<= 1;
     pl.ks = ks;
-    pl.ppw = points_per_wg(ks);
     pl.bk = k_block_rows(ks);
-    pl.tiles = static_cast<int>((N + pl.ppw - 1) / pl.ppw);
-    pl.wgs = pl.tiles;
     const int nkb = static_cast<int>((K + pl.bk - 1) / pl.bk);   // centroid blocks
     const int cus = compute_units > 0 ? compute_units : kDefaultComputeUnits;
+    const int resident = cus * assign_wgs_per_cu(ks);            // workgroups held at once
+    const int wide = wide_point_blocks(ks);
+    auto tiles_for = [&](int pb) {
+        return static_cast<int>((N + points_per_wg(ks, pb) - 1) / points_per_wg(ks, pb));
+    };
 
-    // Too few point tiles to fill the GPU: split K too, aiming at about 3/4
-    // of the workgroups the GPU holds at once, with at least two centroid
-    // blocks per K-range (the merge pass and the extra launch cost ~10 us,
-    // which a one-block range does not earn back).  Measured at N = 65536
-    // (median us): D=64 K=4096: 2 ranges 72, 3: 66, 4: 85; D=64 K=16384:
-    // 2: 187, 3: 166, 4: 171; D=128 K=4096: 2: 76, 3: 92; D=128 K=16384:
-    // 2: 223, 3: 271; K=512 (two blocks): direct 21, split 30-34.
-    const int target_wgs = 3 * cus * assign_wgs_per_cu(ks) / 4;
+    // Too few wide point tiles to fill the GPU: first try narrow tiles (one
+    // point block per wave) if they fit in one round and K is at most 16
+    // centroid blocks; otherwise split K, aiming at about 3/4 of the
+    // workgroups the GPU holds at once, with at least two centroid blocks per
+    // K-range (the merge pass and the extra launch cost ~10 us, which a
+    // one-block range does not earn back).  Measured at N = 65536 (median
+    // us): D=64 K=4096: wide split 3 54, narrow 45; D=64 K=512: wide 19,
+    // narrow 11; D=64 K=16384: split 3 149, narrow 146; D=128 K=512: wide 21,
+    // narrow 16; D=128 K=4096: split 2 68, narrow 70; D=128 K=16384: split 2
+    // 216, narrow 235, split 3 271; N=4096 D=64 K=256: wide 13, narrow 7.
+    const int target_wgs = 3 * resident / 4;
+    int pb = wide;
+    if (force_path == 1 && force_count == 1)
+        pb = 1;
+    else if (force_path == 0 && tiles_for(wide) < target_wgs && nkb <= 16 &&
+             tiles_for(1) <= resident)
+        pb = 1;
+    pl.pb = pb;
+    pl.ppw = points_per_wg(ks, pb);
+    pl.tiles = tiles_for(pb);
+    pl.wgs = pl.tiles;
+
     int splits = 1;
     if (force_path == 2) {
         splits = force_count > 0 ? force_count : (target_wgs + pl.tiles - 1) / pl.tiles;
         if (splits < 1)
             splits = 1;
-    } else if (force_path == 0 && pl.tiles < target_wgs) {
+    } else if (force_path == 0 && pb == wide && pl.tiles < target_wgs) {
         splits = (target_wgs + pl.tiles - 1) / pl.tiles;
         if (splits > nkb / 2)
             splits = nkb / 2 > 1 ? nkb / 2 : 1;

@@ -130,7 +130,9 @@ def test_plan_for_the_workloads(lib):
     plans = {i: km.kmeans_plan(c["N"], c["D"], c["K"]) for i, c in CONFIGS.items()}
     for i in (3, 4, 5):
         assert plans[i]["path"] == km.PATH_DIRECT and plans[i]["splits"] == 1
-    assert plans[2]["path"] == km.PATH_SPLIT and plans[2]["splits"] > 1
+    assert plans[3]["points_per_wg"] == 512 and plans[4]["points_per_wg"] == 256
+    for i in (1, 2):       # small N: narrow tiles (one 32-point block per wave)
+        assert plans[i]["path"] == km.PATH_DIRECT and plans[i]["points_per_wg"] == 128
     for i, c in CONFIGS.items():
         p = plans[i]
         assert p["padded_d"] >= c["D"] and p["padded_d"] % 16 == 0
@@ -138,31 +140,36 @@ def test_plan_for_the_workloads(lib):
         assert p["splits"] * p["k_block"] >= 1
 
 
-# Dispatch on the pages' 13 shapes for a 256-CU GPU (measured choices: the
-# split path only where the point tiles leave the GPU part idle and every
-# K-range keeps at least two centroid blocks).
+# Dispatch on the pages' 13 shapes for a 256-CU GPU, as (path, K-ranges,
+# points per workgroup): narrow tiles where N alone cannot fill the GPU and K
+# is at most 16 centroid blocks, the K-split above that, wide tiles at large N.
 SWEEP_PLANS = {
-    (65536, 64, 512): (1, 1), (65536, 64, 4096): (2, 3), (65536, 64, 16384): (2, 3),
-    (65536, 128, 512): (1, 1), (65536, 128, 4096): (2, 2), (262144, 128, 4096): (1, 1),
-    (262144, 128, 16384): (1, 1), (1048576, 128, 4096): (1, 1), (65536, 256, 512): (1, 1),
-    (65536, 256, 4096): (1, 1), (262144, 256, 4096): (1, 1), (262144, 256, 16384): (1, 1),
-    (1048576, 256, 4096): (1, 1),
+    (65536, 64, 512): (1, 1, 128), (65536, 64, 4096): (1, 1, 128),
+    (65536, 64, 16384): (2, 3, 512), (65536, 128, 512): (1, 1, 256),
+    (65536, 128, 4096): (1, 1, 256), (262144, 128, 4096): (1, 1, 512),
+    (262144, 128, 16384): (1, 1, 512), (1048576, 128, 4096): (1, 1, 512),
+    (65536, 256, 512): (1, 1, 256), (65536, 256, 4096): (1, 1, 256),
+    (262144, 256, 4096): (1, 1, 256), (262144, 256, 16384): (1, 1, 256),
+    (1048576, 256, 4096): (1, 1, 256),
 }
 
 
 def test_plan_for_the_sweep_shapes(lib):
     from means_nearest_centroid_amd.workloads import SWEEP_SHAPES
     assert set(SWEEP_SHAPES) == set(SWEEP_PLANS)
-    for shape, (path, splits) in SWEEP_PLANS.items():
+    for shape, want in SWEEP_PLANS.items():
         p = km.kmeans_plan(*shape, 256)
-        assert (p["path"], p["splits"]) == (path, splits), shape
+        assert (p["path"], p["splits"], p["points_per_wg"]) == want, shape
         assert km.kmeans_plan(*shape) == p      # 0 CUs: the MI355X default
 
 
 def test_plan_follows_the_compute_unit_count(lib):
-    assert km.kmeans_plan(65536, 128, 4096, 256)["path"] == km.PATH_SPLIT
-    assert km.kmeans_plan(65536, 128, 4096, 128)["path"] == km.PATH_DIRECT
-    assert km.kmeans_plan(65536, 128, 4096, 1024)["splits"] == 6
+    assert km.kmeans_plan(65536, 128, 16384, 256)["splits"] == 2
+    assert km.kmeans_plan(65536, 128, 16384, 128)["path"] == km.PATH_DIRECT
+    assert km.kmeans_plan(65536, 128, 16384, 1024)["splits"] == 6
+    # narrow tiles only when they fit in one round
+    assert km.kmeans_plan(65536, 64, 4096, 256)["points_per_wg"] == 128
+    assert km.kmeans_plan(65536, 64, 4096, 64)["points_per_wg"] == 512
 
 
 @pytest.mark.parametrize("N,D,K", [(1, 16, 1), (100, 80, 7), (5000, 192, 3000),

@@ -70,8 +70,9 @@ SMALL = [  # (N, D, K): ragged tails in every dimension, several tiles
 
 
 @pytest.mark.parametrize("path,count", [(km.PATH_AUTO, 0), (km.PATH_DIRECT, 0),
-                                        (km.PATH_SPLIT, 0), (km.PATH_SPLIT, 3)],
-                         ids=["auto", "direct", "split", "split3"])
+                                        (km.PATH_DIRECT, 1), (km.PATH_SPLIT, 0),
+                                        (km.PATH_SPLIT, 3)],
+                         ids=["auto", "wide", "narrow", "split", "split3"])
 @pytest.mark.parametrize("N,D,K", SMALL)
 def test_small_shapes(N, D, K, path, count):
     X, C, _ = W.gaussian_mixture(N, D, K, 1000 + N + K)
@@ -179,7 +180,8 @@ def test_nonfinite_centroids():
     X[10, 3] = W.BF16_PINF
     X[11, 4] = W.BF16_NINF
     X[12, 5] = W.BF16_QNAN
-    for path, count in ((km.PATH_DIRECT, 0), (km.PATH_SPLIT, 0), (km.PATH_SPLIT, 3)):
+    for path, count in ((km.PATH_DIRECT, 0), (km.PATH_DIRECT, 1), (km.PATH_SPLIT, 0),
+                        (km.PATH_SPLIT, 3)):
         lab, md = run(X, C, path, count)
         parity.check(X, C, lab, md)
 
@@ -250,6 +252,18 @@ def test_split_equals_direct_bitwise(N, D, K):
         ls, md_s = run(X, C, km.PATH_SPLIT, splits)
         assert np.array_equal(ld, ls)
         assert md_d.tobytes() == md_s.tobytes()
+
+
+@pytest.mark.parametrize("N,D,K", [(5000, 64, 4096), (3000, 128, 700), (2500, 16, 1000),
+                                   (700, 48, 300), (1100, 256, 129), (70000, 64, 600)])
+def test_narrow_tiles_equal_wide_bitwise(N, D, K):
+    """Narrow point tiles only regroup points over workgroups: every score,
+    and so every output, is bitwise that of the wide tiles."""
+    X, C, _ = W.gaussian_mixture(N, D, K, 120 + D)
+    lw, mw = run(X, C, km.PATH_DIRECT, 0)
+    ln, mn = run(X, C, km.PATH_DIRECT, 1)
+    assert np.array_equal(lw, ln)
+    assert mw.tobytes() == mn.tobytes()
 
 
 def test_deterministic_repeat():

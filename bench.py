@@ -313,8 +313,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the assignment library has no "
+              "multi-GPU mode (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     if args.sweep:

@@ -214,6 +214,26 @@ def test_zero_and_signed_zero_points():
     assert lab[0] == lab[1]
 
 
+def test_denormal_inputs():
+    """bf16 denormals in points and centroids (exponent bits zero): products
+    of them underflow in fp32, so scores tie or nearly tie; the outputs must
+    still satisfy the acceptance rule and be finite."""
+    rng = np.random.default_rng(83)
+    X, C, _ = W.gaussian_mixture(500, 64, 90, 83)
+    X = X.copy()
+    C = C.copy()
+    den_x = rng.integers(1, 0x80, size=X.shape).astype(np.uint16) | (
+        rng.integers(0, 2, size=X.shape).astype(np.uint16) << 15)
+    den_c = rng.integers(1, 0x80, size=C.shape).astype(np.uint16)
+    X[:100] = den_x[:100]                       # all-denormal points
+    X[100:200, ::3] = den_x[100:200, ::3]       # some denormal coordinates
+    C[:30] = den_c[:30]                         # all-denormal centroids
+    C[30:60, ::2] = den_c[30:60, ::2]
+    lab, md = run(X, C)
+    assert np.all(np.isfinite(md))
+    parity.check(X, C, lab, md)
+
+
 def test_single_centroid():
     X, C, _ = W.gaussian_mixture(1000, 128, 1, 79)
     lab, md = run(X, C)

@@ -162,28 +162,29 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, KM_LDS void *dst
 #endif
 }
 
-// One workgroup = 4 waves; wave w owns P blocks of 32 points.  Grid:
-// x = point workgroups, y = K-ranges of k_chunk centroids.
+// One workgroup = WAVES waves (4, or 8 at D = 128 and 256 so that one
+// centroid stream per CU feeds two waves per SIMD); wave w owns P blocks of
+// 32 points.  Grid: x = point workgroups, y = K-ranges of k_chunk centroids.
 //
 // Data movement.  Centroid rows stream through two LDS stages in blocks of
 // BK rows.  Each block is copied global -> LDS by buffer_load ... lds (no
 // staging registers); its norms go through one register per thread.  One
 // barrier per block, at the start of the block's last tile, publishes the
-// next block; by then every wave has also finished reading the current
-// block's stage (the last tile's fragments were read one tile earlier), so
-// the DMA for the block after next goes into that stage right behind the
-// barrier and has a whole block of compute to land.  The two stages are
-// distinct arrays and the block loop is unrolled by two, so the compiler can
-// tell a ds_read of one stage from a DMA into the other and does not wait
-// on the DMA.
+// next block (each wave first waits for its own DMAs); by then every wave
+// has also finished reading the current block's stage (the last tile's
+// fragments were read one tile earlier), so the DMA for the block after next
+// goes into that stage right behind the barrier and has a whole block of
+// compute to land.  The two stages are distinct arrays and the block loop is
+// unrolled by two, so the compiler can tell a ds_read of one stage from a
+// DMA into the other and does not wait on the DMA.
 //
 // Per tile (32 centroid rows) a wave issues P*KS MFMAs; right after the last
 // MFMA that reads A fragment ks, the fragment of the NEXT tile is read into
 // the same registers, so LDS latency hides behind the MFMA chain.
 //
-// Epilogue per (tile, point block), per lane (16 scores of one point):
+// Reduction per (tile, point block), per lane (16 scores of one point):
 //   m = min(best, s_0..s_15)           8 v_min3 (NaN inputs are ignored)
-//   if m < best (strict; rare after the first tiles):
+//   if m < best (strict; taken less and less often as K advances):
 //       slot = lowest r with s_r == m  (inline-constant selects)
 //       best = m, best_tile = tile, best_slot = slot
 // m is always one of its inputs, so the winner is exact; a strict '<' keeps
@@ -314,38 +315,45 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         }
     };
 
-    // With several point blocks per wave, every reduction reads MFMA results
-    // issued a whole chain earlier: point block p's MFMAs are issued, then
+    // Every reduction reads MFMA results issued a whole chain earlier.  With
+    // several point blocks per wave, point block p's MFMAs are issued, then
     // block p-1 is reduced while they run (the previous tile's last block
-    // after the first block of this tile; its slot holds +inf before the
-    // first tile).  With one point block a tile is reduced right after its
-    // own MFMAs (a second accumulator does not fit the register budget) and
-    // the other wave of the SIMD keeps the matrix pipe busy meanwhile.
-    constexpr bool ROTATE = P > 1;
-    f32x16 acc[P];
-    if (ROTATE) {
+    // after the first block of this tile).  With one block per wave, two
+    // accumulator sets alternate between tiles and the previous tile is
+    // reduced while this one's MFMAs run.  The set read first holds +inf.
+    // At D >= 256 the second set does not fit the register budget: a tile is
+    // reduced right after its own MFMAs and the other wave of the SIMD keeps
+    // the matrix pipe busy meanwhile.
+    constexpr int NACC = P > 1 ? P : (KS <= 8 ? 2 : 1);
+    static_assert(NACC != 2 || P > 1 || TB % 2 == 0, "tile parity must repeat in every block");
+    f32x16 acc[NACC];
+    if (NACC > 1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            acc[P - 1][r] = INFINITY;
+            acc[NACC - 1][r] = INFINITY;
     }
-    // One tile: MFMAs with the current operands (a, ninit), whose registers
-    // are refilled with the next tile's fragments right after their last
-    // use, interleaved with the reductions.
-    auto tile = [&](const uint8_t *next_c, const float *next_n, int next_r0, int kt) KM_INLINE {
+    // One tile (j-th of its block, first centroid kt): MFMAs with the
+    // current operands (a, ninit), whose registers are refilled with the next
+    // tile's fragments right after their last use, interleaved with the
+    // reductions.
+    auto tile = [&](const uint8_t *next_c, const float *next_n, int next_r0, int kt, int j) KM_INLINE {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
+            f32x16 &dst = acc[P > 1 ? p : (NACC == 2 ? (j & 1) : 0)];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), ks == 0 ? ninit : acc[p], 0, 0, 0);
+                dst = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), ks == 0 ? ninit : dst, 0, 0, 0);
                 if (p == P - 1) {
                     a[ks] = read_a(next_c, next_r0, ks);
                     if (ks == 0)
                         ninit = read_n(next_n, next_r0);
                 }
             }
-            if (!ROTATE)
+            if (NACC == 1)
                 reduce(0, acc[0], kt);
+            else if (P == 1)
+                reduce(0, acc[(j + 1) & 1], kt - kTileRows);
             else if (p == 0)
                 reduce(P - 1, acc[P - 1], kt - kTileRows);
             else
@@ -403,7 +411,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
             if (j + 1 < TB) {
-                tile(cc, nc, (j + 1) * kTileRows, kb + j * kTileRows);
+                tile(cc, nc, (j + 1) * kTileRows, kb + j * kTileRows, j);
             } else {
                 if (b + 1 < nblocks) {
                     write_norm(nn);
@@ -414,7 +422,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                         load_norm(b + 2);
                     }
                 }
-                tile(cn, nn, 0, kb + j * kTileRows);
+                tile(cn, nn, 0, kb + j * kTileRows, j);
             }
         }
     };
@@ -424,8 +432,9 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
             break;
         do_block(b + 1, c_st1, n_st1, c_st0, n_st0);
     }
-    if (ROTATE)   // the last tile's last point block
-        reduce(P - 1, acc[P - 1], k_begin + (nblocks - 1) * BK + (TB - 1) * kTileRows);
+    if (NACC > 1)   // the last tile's last point block
+        reduce(P - 1, acc[P > 1 ? P - 1 : ((TB - 1) & 1)],
+               k_begin + (nblocks - 1) * BK + (TB - 1) * kTileRows);
 
     // ---- merge the two lanes that hold the same point ----
 #pragma unroll

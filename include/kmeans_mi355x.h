@@ -130,8 +130,10 @@ kmeans_status_t kmeans_assign_path(const void *X, const void *C, const float *no
  * pointer may be NULL.
  *   path          KMEANS_PATH_DIRECT or KMEANS_PATH_SPLIT
  *   splits        number of K-ranges (1 on the direct path)
- *   workgroups    point-workgroups per K-range (grid x)
- *   points_per_wg points owned by one workgroup
+ *   workgroups    point-workgroups per K-range, over all launches (when
+ *                 the last round of point tiles would be mostly empty, its
+ *                 points run as a second launch of narrow tiles)
+ *   points_per_wg points owned by one workgroup of the first launch
  *   k_block       centroid rows staged in LDS per block
  *   padded_d      D rounded up to the kernel's k-step multiple
  */

@@ -100,8 +100,20 @@ kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int
     const int n = static_cast<int>(N), d = static_cast<int>(D), k = static_cast<int>(K);
 
     if (pl.path == KMEANS_PATH_DIRECT) {
-        hipError_t e = kmeans::launch_assign(pl, Xb, Cb, norms, n, d, k, labels, min_dist,
+        const int head = n - pl.tail_points;
+        hipError_t e = kmeans::launch_assign(pl, Xb, Cb, norms, head, d, k, labels, min_dist,
                                              nullptr, nullptr, nullptr, stream);
+        if (e == hipSuccess && pl.tail_points > 0) {
+            // The last points as narrow tiles: same kernel family on offset
+            // pointers, so each point's result is computed exactly as before.
+            kmeans::Plan tp = pl;
+            tp.pb = 1;
+            tp.ppw = pl.ppw / kmeans::wide_point_blocks(pl.ks);
+            tp.tiles = tp.wgs = pl.tail_wgs;
+            e = kmeans::launch_assign(tp, Xb + static_cast<size_t>(head) * D, Cb, norms,
+                                      pl.tail_points, d, k, labels + head, min_dist + head,
+                                      nullptr, nullptr, nullptr, stream);
+        }
         if (e != hipSuccess)
             return fail(KMEANS_ERR_HIP, "assign launch failed: %s", hipGetErrorString(e));
         return ok();
@@ -186,7 +198,7 @@ kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_uni
     if (splits)
         *splits = pl.splits;
     if (workgroups)
-        *workgroups = N > 0 ? pl.wgs : 0;
+        *workgroups = N > 0 ? pl.wgs + pl.tail_wgs : 0;
     if (points_per_wg)
         *points_per_wg = pl.ppw;
     if (k_block)

@@ -53,6 +53,11 @@ struct Plan {
     int ppw;           // points per workgroup
     int bk;            // centroid rows per LDS block
     int k_chunk;       // centroids per K-range, multiple of bk
+    // Direct path only: the last tail_points points run as a second launch of
+    // narrow tiles (tail_wgs workgroups) so that a partial last round of wide
+    // tiles does not hold the whole GPU; the first launch covers the rest.
+    int tail_points;   // 0: one launch
+    int tail_wgs;
 };
 
 // force_path: 0 auto, 1 direct, 2 split; force_count: K-ranges (split) or

@@ -635,6 +635,25 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
         pl.splits = 1;
         pl.k_chunk = nkb * pl.bk;
     }
+
+    // Wave tail: wide tiles that fill only part of their last round (at most
+    // half of it at D = 128, a quarter at D <= 64) take as long as a full
+    // round.  Their points run instead as one round of narrow tiles, each
+    // about half as long, in a second launch (measured: N = 300000 and
+    // 600000 at D = 128, K = 4096).
+    pl.tail_points = 0;
+    pl.tail_wgs = 0;
+    if (force_path == 0 && pl.path == 1 && pb == wide && wide > 1 && pl.tiles > resident) {
+        const int rem = pl.tiles % resident;
+        const int64_t tail = N - static_cast<int64_t>(pl.tiles - rem) * pl.ppw;
+        const int64_t narrow_tiles = (tail + points_per_wg(ks, 1) - 1) / points_per_wg(ks, 1);
+        if (rem > 0 && narrow_tiles <= resident) {
+            pl.tail_points = static_cast<int>(tail);
+            pl.tail_wgs = static_cast<int>(narrow_tiles);
+            pl.tiles -= rem;
+            pl.wgs = pl.tiles;
+        }
+    }
     return pl;
 }
 

@@ -286,6 +286,25 @@ def test_narrow_tiles_equal_wide_bitwise(N, D, K):
     assert mw.tobytes() == mn.tobytes()
 
 
+@pytest.mark.parametrize("N,D,K", [(300000, 128, 520), (262244, 128, 300), (270000, 64, 700)])
+def test_wave_tail_launch_equals_wide_bitwise(N, D, K):
+    """A partial last round of wide tiles runs as a second launch of narrow
+    tiles on offset pointers; outputs must be bitwise those of one wide
+    launch, and correct around the boundary between the two launches."""
+    plan = km.kmeans_plan(N, D, K)
+    wide = 512
+    head = (N // wide // 256) * 256 * wide if D == 128 else (N // wide // 512) * 512 * wide
+    assert plan["workgroups"] > head // wide        # a tail launch is planned
+    X, C, _ = W.gaussian_mixture(N, D, K, 130 + D)
+    la, ma = run(X, C)
+    lw, mw = run(X, C, km.PATH_DIRECT, 0)
+    assert np.array_equal(la, lw)
+    assert ma.tobytes() == mw.tobytes()
+    idx = np.unique(np.concatenate([np.arange(head - 64, min(N, head + 64)),
+                                    parity.sample_indices(N, 131, 256, 512, 64)]))
+    parity.check(X, C, la, ma, idx=idx)
+
+
 def test_deterministic_repeat():
     X, C, _ = W.make_config(2, 29)
     a = run(X, C)

@@ -90,7 +90,10 @@ kmeans_status_t kmeans_centroid_norms(const void *C, int64_t K, int64_t D,
  *             this C (other values give the scores n_k - 2 x.c_k as passed).
  *   N         number of points, 0 <= N < 2^31 (N == 0: no-op, KMEANS_OK).
  *   D         feature dimension, 16 <= D <= 512, D % 16 == 0.
- *   K         number of centroids, 1 <= K < 2^31.
+ *   K         number of centroids, 1 <= K < 2^31, with C at most 64 x 2 GiB
+ *             (larger: KMEANS_ERR_UNSUPPORTED).  Centroids over 2 GiB always
+ *             run the K-split path (kmeans_assign_path with
+ *             KMEANS_PATH_DIRECT then returns KMEANS_ERR_UNSUPPORTED).
  *   labels    int32 [N], written: lowest index minimising s_ik.
  *   min_dist  fp32 [N], written: squared distance to the chosen centroid,
  *             max(0, ||x||^2 + s_best) for finite data.

@@ -70,6 +70,9 @@ kmeans_status_t check_shape(int64_t N, int64_t D, int64_t K) {
         return fail(KMEANS_ERR_UNSUPPORTED, "N=%lld or K=%lld too large (max %lld)",
                     static_cast<long long>(N), static_cast<long long>(K),
                     static_cast<long long>(kMaxRows));
+    if (kmeans::min_k_ranges(D, K) > kmeans::kMaxSplits)
+        return fail(KMEANS_ERR_UNSUPPORTED, "K=%lld rows of D=%lld: centroids over %d x 2 GiB",
+                    static_cast<long long>(K), static_cast<long long>(D), kmeans::kMaxSplits);
     return KMEANS_OK;
 }
 
@@ -83,6 +86,9 @@ kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int
         return fail(KMEANS_ERR_INVALID_ARG, "path=%d unknown", path);
     if (count < 0)
         return fail(KMEANS_ERR_INVALID_ARG, "count=%d must be >= 0", count);
+    if (kmeans::min_k_ranges(D, K) > 1 && path == KMEANS_PATH_DIRECT)
+        return fail(KMEANS_ERR_UNSUPPORTED, "K=%lld rows of D=%lld: centroids over 2 GiB need "
+                    "the split path", static_cast<long long>(K), static_cast<long long>(D));
     if (N == 0)
         return ok();
     if (!X || !C || !norms || !labels || !min_dist)

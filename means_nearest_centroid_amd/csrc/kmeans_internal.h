@@ -11,6 +11,9 @@ constexpr int kThreads = 256;        // norms / merge kernels: 4 wave64s
 constexpr int kTileRows = 32;        // centroid rows per MFMA tile (A operand)
 constexpr int kTileCols = 32;        // points per MFMA tile (B operand)
 constexpr int kMaxSplits = 64;
+// Bytes of centroid rows one K-range may span: buffer resources hold a
+// 32-bit size, and offsets at or past 2^31 stand for "out of range".
+constexpr int64_t kMaxRangeBytes = (int64_t(1) << 31) - (int64_t(1) << 16);
 constexpr int32_t kNoLabel = 0x7fffffff;
 
 // Kernel shape for a padded feature width of 16*ks (ks a power of two).
@@ -59,6 +62,10 @@ struct Plan {
     int tail_points;   // 0: one launch
     int tail_wgs;
 };
+
+// K-ranges needed so that none spans more than kMaxRangeBytes of centroid
+// rows (1 unless C is over 2 GiB); more than kMaxSplits is unsupported.
+int min_k_ranges(int64_t D, int64_t K);
 
 // force_path: 0 auto, 1 direct, 2 split; force_count: K-ranges (split) or
 // point blocks per wave (direct: 1 narrow, other wide), 0 auto;

@@ -574,6 +574,17 @@ hipError_t launch_merge(const Plan &pl, const uint16_t *X, const uint16_t *C,
     return hipGetLastError();
 }
 
+int min_k_ranges(int64_t D, int64_t K) {
+    int ks = 1;
+    while (ks * 16 < D)
+        ks <<= 1;
+    const int64_t bk = k_block_rows(ks);
+    const int64_t cap_blocks = kMaxRangeBytes / (D * 2) / bk;   // whole blocks per range
+    const int64_t nkb = (K + bk - 1) / bk;
+    const int64_t r = (nkb + cap_blocks - 1) / cap_blocks;
+    return r > kMaxSplits ? kMaxSplits + 1 : static_cast<int>(r);
+}
+
 Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
                int compute_units) {
     Plan pl{};
@@ -623,6 +634,9 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
         if (splits > nkb / 2)
             splits = nkb / 2 > 1 ? nkb / 2 : 1;
     }
+    const int need = min_k_ranges(D, K);   // C over 2 GiB: split regardless
+    if (splits < need)
+        splits = need;
     if (splits > kMaxSplits)
         splits = kMaxSplits;
     if (splits > nkb)
@@ -630,7 +644,7 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
     const int blocks_per_split = (nkb + splits - 1) / splits;
     pl.k_chunk = blocks_per_split * pl.bk;
     pl.splits = static_cast<int>((K + pl.k_chunk - 1) / pl.k_chunk);
-    pl.path = (force_path == 2 || (force_path == 0 && pl.splits > 1)) ? 2 : 1;
+    pl.path = (force_path == 2 || (force_path == 0 && pl.splits > 1) || need > 1) ? 2 : 1;
     if (pl.path == 1) {
         pl.splits = 1;
         pl.k_chunk = nkb * pl.bk;

@@ -184,6 +184,21 @@ def test_plan_covers_every_point_and_centroid(lib, N, D, K):
         assert p["splits"] == 1
 
 
+def test_centroids_over_2gib_are_split_or_refused(lib):
+    # 2,100,000 rows of 1 KiB exceed one 2 GiB K-range: split, never direct.
+    p = km.kmeans_plan(64, 512, 2100000)
+    assert p["path"] == km.PATH_SPLIT and p["splits"] >= 2
+    assert km.kmeans_plan(64, 512, 2000000)["path"] == km.PATH_SPLIT   # small N anyway
+    st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 512, 2100000, FAKE, FAKE,
+                                km.PATH_DIRECT, 0, NUL)
+    assert st == km.KMEANS_ERR_UNSUPPORTED
+    # Over 64 ranges of 2 GiB: unsupported on every path.
+    with pytest.raises(km.KmeansError):
+        km.kmeans_plan(64, 512, 200000000)
+    st = lib.kmeans_assign(FAKE, FAKE, FAKE, 10, 512, 200000000, FAKE, FAKE, NUL)
+    assert st == km.KMEANS_ERR_UNSUPPORTED
+
+
 def test_plan_rejects_bad_shapes(lib):
     with pytest.raises(km.KmeansError):
         km.kmeans_plan(10, 72, 5)

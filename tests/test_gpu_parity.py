@@ -256,6 +256,28 @@ def test_maximum_d_and_large_k():
     parity.check(X, C, lab, md)
 
 
+def test_centroids_over_2gib():
+    """70M centroid rows of D=16 (2.24 GB) at a large N: one buffer resource
+    would exceed its 32-bit range, so the plan splits K.  Every row is a far
+    constant except 256 near rows at the start and 256 past the 2 GiB mark,
+    so the oracle needs only the distinct rows."""
+    N, D, K = 262144, 16, 70_000_000
+    plan = km.kmeans_plan(N, D, K)
+    assert plan["path"] == km.PATH_SPLIT and plan["splits"] >= 2
+    X, near, _ = W.gaussian_mixture(N, D, 512, 140)
+    far = W.f32_to_bf16_bits(np.full(D, 40.0, np.float32))
+    C = np.empty((K, D), np.uint16)
+    C[:] = far
+    C[:256] = near[:256]
+    C[K - 256:] = near[256:]
+    lab, md = run(X, C)
+    del C
+    mapped = np.where(lab < 256, lab + 1, np.where(lab >= K - 256, lab - (K - 256) + 257, 0))
+    C_eff = np.vstack([far[None, :], near])
+    parity.check(X, C_eff, mapped, md, idx=parity.sample_indices(N, 141, 1024, 2048, 64))
+    assert np.count_nonzero(lab >= K - 256) > N // 4     # the far end of C was read
+
+
 def test_large_k_small_n():
     X, C, _ = W.gaussian_mixture(300, 64, 70000, 82)
     lab, md = run(X, C)

@@ -27,8 +27,9 @@
 //    index can only enter a v_cndmask as a VGPR or an inline constant, so a
 //    per-score (score, index) update costs 3+ VALU ops.  Instead each tile is
 //    reduced to its minimum with v_min3 (half an op per score) and the exact
-//    slot is searched only when that minimum beats the running best, which
-//    becomes rare once a point has seen its nearest centroids.  Ties keep the
+//    slot is searched only when that minimum beats the running best: about
+//    ln(K) times per point over a scan, though a wave (64 lanes) still takes
+//    that branch on most tiles early in K and fewer later.  Ties keep the
 //    lower index at every level; the two lanes that share a point merge by
 //    (score, index) ("Deterministic winner merge").  The N x K score matrix
 //    never leaves registers.
@@ -139,7 +140,10 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past num_records
+// An offset past every buffer's num_records: point tiles span at most 512
+// KiB and a K-range at most kMaxRangeBytes (< 2^31) of centroid rows.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+static_assert(kMaxRangeBytes < kOutOfRange, "K-range cap must leave the marker out of range");
 
 #define KM_LDS __attribute__((address_space(3)))
 // The assign kernel's lambdas must be inlined before its arrays (resident

@@ -1,9 +1,9 @@
 """HIP path against the fp64 oracle, through the C ABI, on an MI355X.
 
-Small shapes (ragged in N, K and D, spanning several tiles) are checked on
-every point; the five workloads run at their full sizes with the production
-dispatch and are checked on every point (workloads 1-2) or on a sample of
-points plus every structured point (3-5).  Acceptance rule: ``parity.py``.
+Small shapes (ragged in N, K and D, spanning several tiles) and the five
+workloads, at their full sizes with the production dispatch, are checked on
+every point; the 13 benchmark shapes on samples.  Acceptance rule:
+``parity.py``.
 """
 
 import os
@@ -88,30 +88,24 @@ def test_workload1_full(seed):
     assert st["bad_strict"] == 0
 
 
-def test_workload2_full():
-    X, C, _ = W.make_config(2, 17)
+@pytest.mark.parametrize("seed", W.SEEDS)
+def test_workload2_full(seed):
+    X, C, _ = W.make_config(2, seed)
     lab, md = run(X, C)
     parity.check(X, C, lab, md)
 
 
-@pytest.mark.parametrize("seed", [29, 43])
-def test_workload2_sampled(seed):
-    X, C, _ = W.make_config(2, seed)
-    lab, md = run(X, C)
-    parity.check(X, C, lab, md, idx=parity.sample_indices(X.shape[0], seed, 1024, 1024))
-
-
 @pytest.mark.parametrize("seed", W.SEEDS)
-def test_workload3_sampled(seed):
+def test_workload3_full(seed):
     X, C, _ = W.make_config(3, seed)
     lab, md = run(X, C)
-    parity.check(X, C, lab, md, idx=parity.sample_indices(X.shape[0], seed, 1024, 1024))
+    parity.check(X, C, lab, md)
 
 
-def test_workload4_sampled():
+def test_workload4_full():
     X, C, _ = W.make_config(4, 17)
     lab, md = run(X, C)
-    parity.check(X, C, lab, md, idx=parity.sample_indices(X.shape[0], 4, 1024, 1024))
+    parity.check(X, C, lab, md)
 
 
 # The pages' 13 benchmark shapes.  The pages checked the first 2048
@@ -136,10 +130,9 @@ def workload5():
     return X, C, meta, lab, md
 
 
-def test_workload5_sampled(workload5):
+def test_workload5_full(workload5):
     X, C, meta, lab, md = workload5
-    N = X.shape[0]
-    parity.check(X, C, lab, md, idx=parity.sample_indices(N, 5, 0, 2048, 4096 + 64))
+    parity.check(X, C, lab, md)
 
 
 def test_workload5_nan_slice(workload5):

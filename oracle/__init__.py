@@ -46,8 +46,12 @@ def load(path: str = LIBRARY):
     lib.oracle_score_for.argtypes = [u16p, u16p, i64, i64, i32p, f64p]
     lib.oracle_sqdist_for.argtypes = [u16p, u16p, i64, i64, i32p, f64p]
     lib.oracle_all_scores.argtypes = [u16p, u16p, i64, i64, i64, f64p]
+    i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+    lib.oracle_update.argtypes = [u16p, i32p, u16p, i64, i64, i64, i64p, f64p, u16p]
+    lib.oracle_bf16_from_double_array.argtypes = [f64p, i64, u16p]
     for f in ("oracle_centroid_norms", "oracle_assign", "oracle_score_for",
-              "oracle_sqdist_for", "oracle_all_scores"):
+              "oracle_sqdist_for", "oracle_all_scores", "oracle_update",
+              "oracle_bf16_from_double_array"):
         getattr(lib, f).restype = None
     return lib
 
@@ -120,3 +124,30 @@ def all_scores(X, C, lib=None) -> np.ndarray:
     out = np.empty((X.shape[0], C.shape[0]), dtype=np.float64)
     (lib or _get()).oracle_all_scores(X, C, X.shape[0], X.shape[1], C.shape[0], out)
     return out
+
+
+def bf16_from_double(a, lib=None) -> np.ndarray:
+    """fp64 values -> bf16 bit patterns (nearest, ties to even)."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    (lib or _get()).oracle_bf16_from_double_array(a.ravel(), a.size, out.ravel())
+    return out
+
+
+def update(X, labels, C_old, lib=None) -> dict:
+    """Centroid update from ``labels``: per-cluster counts (int64), fp64
+    means ``[K][D]`` and the new bf16 centroids ``[K][D]`` (an empty
+    cluster keeps its old row; labels outside ``[0, K)`` are ignored)."""
+    X, C_old = _bits(X), _bits(C_old)
+    N, D = X.shape
+    K = C_old.shape[0]
+    if C_old.shape[1] != D:
+        raise ValueError("X and C disagree on D")
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    if labels.shape != (N,):
+        raise ValueError("labels must have one entry per point")
+    counts = np.zeros(K, dtype=np.int64)
+    means = np.zeros((K, D), dtype=np.float64)
+    C_new = np.zeros((K, D), dtype=np.uint16)
+    (lib or _get()).oracle_update(X, labels, C_old, N, D, K, counts, means, C_new)
+    return dict(counts=counts, means=means, C_new=C_new)

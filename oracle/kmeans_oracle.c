@@ -1,5 +1,6 @@
 /*
- * kmeans_oracle.c -- plain CPU oracle for the k-means assignment step.
+ * kmeans_oracle.c -- plain CPU oracle for the k-means assignment step and
+ * the centroid update that follows it.
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU
  * baseline leg of the benchmark may load this library.  It shares no code,
@@ -201,6 +202,89 @@ void oracle_all_scores(const uint16_t *X, const uint16_t *C, int64_t N, int64_t 
                 dot += widen_bf16(X[i * D + j]) * c;
             }
             S[i * K + k] = n - 2.0 * dot;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Centroid update (the step of a Lloyd iteration that follows assignment).
+ *
+ * The pages describe the assignment step only (Summary); they say nothing
+ * about recomputing centroids.  The plain definition is used:
+ *
+ *     count_k = #{ i : labels_i == k }
+ *     mean_k  = (sum of x_i over those i) / count_k     (fp64, point order)
+ *     c'_k    = mean_k rounded to bf16 (nearest, ties to even)  if count_k > 0
+ *     c'_k    = c_k unchanged (bit for bit)                      if count_k == 0
+ *
+ * Readings where the definition leaves a choice: an empty cluster keeps its
+ * centroid; a label outside [0, K) counts for no cluster; sums follow IEEE
+ * arithmetic (a NaN coordinate makes that coordinate of the mean NaN).
+ * ------------------------------------------------------------------------ */
+
+/* fp64 -> bf16 bits, rounding to nearest with ties to even.  bf16 keeps 8
+ * significant bits and the binary32 exponent range: below 2^-126 the spacing
+ * is fixed at 2^-133 (subnormals); results past the largest finite bf16
+ * after rounding become infinite; NaN becomes a quiet NaN of the same sign. */
+uint16_t oracle_bf16_from_double(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0)
+        return sign;
+    int e = ilogb(a);                      /* 2^e <= a < 2^(e+1) */
+    if (e < -126)
+        e = -126;                          /* subnormal range: fixed spacing */
+    double q = ldexp(a, 7 - e);            /* exact scaling; q < 256 */
+    double r = nearbyint(q);               /* default mode: ties to even */
+    double m = ldexp(r, e - 7);
+    const double largest = ldexp(255.0, 120);   /* (2 - 2^-7) * 2^127 */
+    if (m > largest)
+        return (uint16_t)(sign | 0x7F80u);
+    float f = (float)m;                    /* exact: 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+void oracle_bf16_from_double_array(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_from_double(v[i]);
+}
+
+/* counts [K], means [K][D] (fp64; an empty cluster's row is its old
+ * centroid widened) and C_new [K][D] (bf16 bits). */
+void oracle_update(const uint16_t *X, const int32_t *labels, const uint16_t *C_old,
+                   int64_t N, int64_t D, int64_t K, int64_t *counts, double *means,
+                   uint16_t *C_new)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        counts[k] = 0;
+        for (int64_t j = 0; j < D; ++j)
+            means[k * D + j] = 0.0;
+    }
+    for (int64_t i = 0; i < N; ++i) {
+        int64_t k = labels[i];
+        if (k < 0 || k >= K)
+            continue;
+        counts[k] += 1;
+        for (int64_t j = 0; j < D; ++j)
+            means[k * D + j] += widen_bf16(X[i * D + j]);
+    }
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t j = 0; j < D; ++j) {
+            if (counts[k] > 0) {
+                means[k * D + j] /= (double)counts[k];
+                C_new[k * D + j] = oracle_bf16_from_double(means[k * D + j]);
+            } else {
+                means[k * D + j] = widen_bf16(C_old[k * D + j]);
+                C_new[k * D + j] = C_old[k * D + j];
+            }
         }
     }
 }

@@ -253,7 +253,145 @@ def pin_single_centroid(lib):
     assert np.all(r["labels"] == 0) and np.all(np.isnan(r["second"]))
 
 
+# ----------------------------------------------------------------------------
+# Centroid update
+# ----------------------------------------------------------------------------
+
+def exact_bf16_bits(q) -> int:
+    """Round a rational to bf16 (nearest, ties to even), from the format's
+    definition: 8 significant bits, binary32 exponent range, spacing 2^-133
+    below 2^-126, overflow past the largest finite value to infinity."""
+    if q == 0:
+        return 0
+    sign = 0x8000 if q < 0 else 0
+    a = abs(Fraction(q))
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    scaled = a * Fraction(2) ** (7 - e)
+    r = scaled.numerator // scaled.denominator
+    rem = scaled - r
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    value = Fraction(r) * Fraction(2) ** (e - 7)
+    if value > 255 * Fraction(2) ** 120:
+        return sign | 0x7F80
+    f32 = np.array([float(value)], dtype=np.float32)     # exact: 8 bits
+    return sign | int(f32.view(np.uint32)[0] >> 16)
+
+
+def pin_bf16_rounding(lib):
+    """fp64 -> bf16 rounding against exact rational rounding, and against the
+    integer-bit rounding of fp32 values in the input generator."""
+    rng = np.random.default_rng(40)
+    f = (rng.standard_normal(4000) * 2.0 ** rng.integers(-140, 125, 4000)).astype(np.float32)
+    f = f[np.isfinite(f)]
+    got = oracle.bf16_from_double(f.astype(np.float64), lib=lib)
+    assert np.array_equal(got, W.f32_to_bf16_bits(f)), "fp32-representable values"
+    # Values an fp32 intermediate would round twice: just above / below a tie.
+    vals = []
+    for e in (-130, -127, -20, 0, 5, 100, 127):
+        for m in (1, 2, 3, 77, 127):
+            base = Fraction(128 + m) * Fraction(2) ** (e - 7)
+            half = Fraction(1) * Fraction(2) ** (e - 8)
+            for off in (0, Fraction(1) * Fraction(2) ** (e - 40), -Fraction(1) * Fraction(2) ** (e - 40)):
+                vals.append(base + half + off)
+                vals.append(-(base + half + off))
+    vals += [Fraction(2) ** -133, Fraction(3) * Fraction(2) ** -135,
+             Fraction(2) ** -134, Fraction(2) ** -134 + Fraction(2) ** -160,
+             Fraction(255) * Fraction(2) ** 120 + Fraction(2) ** 118,    # rounds down
+             Fraction(511) * Fraction(2) ** 119]                          # tie -> inf
+    d = np.array([float(v) for v in vals])
+    exact = [Fraction(float(v)) for v in vals]     # the fp64 value itself
+    got = oracle.bf16_from_double(d, lib=lib)
+    want = np.array([exact_bf16_bits(v) for v in exact], dtype=np.uint16)
+    assert np.array_equal(got, want), "rational rounding"
+    sp = oracle.bf16_from_double(np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0]), lib=lib)
+    assert list(sp) == [0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x0000, 0x8000], "special values"
+
+
+def update_cases():
+    rng = np.random.default_rng(41)
+    cases = []
+    for seed, (N, D, K) in enumerate([(40, 16, 6), (25, 32, 9), (60, 16, 3)]):
+        X, C, a = W.gaussian_mixture(N, D, K, 200 + seed)
+        lab = a.astype(np.int32)
+        lab[:: 7] = rng.integers(0, K, len(lab[:: 7]))
+        cases.append((X, C, lab))
+    # many binades, a cluster left empty, labels outside [0, K)
+    X = W.f32_to_bf16_bits((rng.standard_normal((30, 16))
+                            * 2.0 ** rng.integers(-12, 12, (30, 16))).astype(np.float32))
+    C = W.f32_to_bf16_bits(rng.standard_normal((5, 16)).astype(np.float32))
+    lab = rng.integers(0, 4, 30).astype(np.int32)      # cluster 4 empty
+    lab[3], lab[11], lab[12] = -1, 5, 1 << 30
+    cases.append((X, C, lab))
+    return cases
+
+
+def pin_update_bruteforce(lib):
+    """Counts, means and bf16 centroids equal the exact rational result."""
+    for X, C, lab in update_cases():
+        r = oracle.update(X, lab, C, lib=lib)
+        K, D = C.shape
+        Xe = [_exact(row) for row in X]
+        for k in range(K):
+            members = [i for i in range(len(lab)) if lab[i] == k]
+            assert r["counts"][k] == len(members), "count"
+            if not members:
+                assert np.array_equal(r["C_new"][k], C[k]), "empty cluster must keep its row"
+                continue
+            for j in range(D):
+                m = sum(Xe[i][j] for i in members) / len(members)
+                assert _rel_close(r["means"][k, j], m, 1e-15), "mean"
+                assert r["C_new"][k, j] == exact_bf16_bits(m), "bf16 mean"
+
+
+def pin_update_closed_forms(lib):
+    """Identical members give that row back bit for bit; a mean of dyadic
+    rows is exact; permuting points changes nothing; scaling by 2^a scales
+    the means exactly; labels from an assignment of C's own rows return C."""
+    X, C, a = W.gaussian_mixture(300, 32, 20, 42)
+    lab = a.astype(np.int32)
+    r = oracle.update(X, lab, C, lib=lib)
+    Xs = C[lab]                                   # every point on its centroid
+    rs = oracle.update(Xs, lab, C, lib=lib)
+    present = np.unique(lab)
+    assert np.array_equal(rs["C_new"][present], C[present]), "identical members"
+    # dyadic rows: the mean of +-1/8 grid points has few bits, so it is exact
+    G = W.dyadic_to_bf16_bits(np.random.default_rng(43).integers(-9, 10, (64, 32)), 3)
+    lg = np.repeat(np.arange(16, dtype=np.int32), 4)
+    rg = oracle.update(G, lg, C[:16], lib=lib)
+    Gf = W.bf16_bits_to_f32(G).astype(np.float64).reshape(16, 4, 32)
+    assert np.array_equal(rg["means"], Gf.mean(1)), "dyadic means"
+    assert np.array_equal(W.bf16_bits_to_f32(rg["C_new"]).astype(np.float64),
+                          Gf.mean(1)), "dyadic bf16"
+    perm = np.random.default_rng(44).permutation(len(lab))
+    rp = oracle.update(X[perm], lab[perm], C, lib=lib)
+    assert np.array_equal(rp["counts"], r["counts"]), "permutation counts"
+    assert np.allclose(rp["means"], r["means"], rtol=1e-15, atol=0), "permutation means"
+    for e in (-4, 3):
+        f = np.float32(2.0 ** e)
+        Xe = W.f32_to_bf16_bits(W.bf16_bits_to_f32(X) * f)
+        Ce = W.f32_to_bf16_bits(W.bf16_bits_to_f32(C) * f)
+        re = oracle.update(Xe, lab, Ce, lib=lib)
+        assert np.array_equal(re["means"], r["means"] * 2.0 ** e), "scaling means"
+        assert np.array_equal(re["C_new"], W.f32_to_bf16_bits(
+            W.bf16_bits_to_f32(r["C_new"]) * f)), "scaling bf16"
+    # Lloyd fixed point: the points are the centroids and assign to themselves.
+    own = oracle.assign(C, C, lib=lib)["labels"]
+    assert np.array_equal(own, np.arange(C.shape[0])), "distinct rows"
+    rf = oracle.update(C, own, C, lib=lib)
+    assert np.array_equal(rf["C_new"], C) and np.all(rf["counts"] == 1), "fixed point"
+    # No points at all: every cluster empty.
+    r0 = oracle.update(X[:0], lab[:0], C, lib=lib)
+    assert np.array_equal(r0["C_new"], C) and not r0["counts"].any(), "no points"
+
+
 ALL_PINS = (pin_bruteforce, pin_centroid_norms, pin_permutation,
             pin_duplicates_and_equal, pin_scaling, pin_exact_member,
             pin_zero_point, pin_one_dimensional, pin_dyadic_ties,
-            pin_nonfinite, pin_single_centroid)
+            pin_nonfinite, pin_single_centroid, pin_bf16_rounding,
+            pin_update_bruteforce, pin_update_closed_forms)

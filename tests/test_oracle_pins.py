@@ -37,6 +37,20 @@ MUTANTS = [
     ("runner_up_not_tracked", "                    sec = b;\n", ""),
     ("norm_not_squared", "            n += c * c;\n        }\n        norms[k] = n;",
      "            n += c;\n        }\n        norms[k] = n;"),
+    # centroid update and its bf16 rounding
+    ("mean_over_all_points", "means[k * D + j] /= (double)counts[k];",
+     "means[k * D + j] /= (double)N;"),
+    ("empty_cluster_zeroed", "C_new[k * D + j] = C_old[k * D + j];", "C_new[k * D + j] = 0;"),
+    ("stray_labels_to_zero", "        if (k < 0 || k >= K)\n            continue;",
+     "        if (k < 0 || k >= K)\n            k = 0;"),
+    ("rounding_truncates", "double r = nearbyint(q);", "double r = floor(q);"),
+    ("ties_away_from_zero", "double r = nearbyint(q);", "double r = round(q);"),
+    ("rounding_through_fp32", "    double q = ldexp(a, 7 - e);",
+     "    a = (double)(float)a;\n    double q = ldexp(a, 7 - e);"),
+    ("subnormal_spacing", "        e = -126;", "        e = -127;"),
+    ("overflow_kept_finite", "        return (uint16_t)(sign | 0x7F80u);\n    float f",
+     "        m = largest;\n    float f"),
+    ("nan_sign_dropped", "        return (uint16_t)(sign | 0x7FC0u);", "        return (uint16_t)0x7FC0u;"),
 ]
 
 

@@ -1,5 +1,6 @@
 /*
- * kmeans_mi355x.h -- C ABI of the MI355X (gfx950) k-means assignment library.
+ * kmeans_mi355x.h -- C ABI of the MI355X (gfx950) k-means assignment library
+ * (with the centroid update that follows assignment in a Lloyd iteration).
  *
  * The operation.  flashlib PR #22, "Optimize Blackwell k-means assignment
  * reduction", Summary: the assignment step scores every (point, centroid)
@@ -31,7 +32,7 @@
  *   - kmeans_last_error() returns a thread-local message for the last
  *     non-OK status on the calling thread.
  *   - Results are bitwise deterministic for identical inputs and shape; no
- *     reduction uses atomics.
+ *     floating-point value is accumulated with atomics.
  *   - Outputs must not overlap inputs (not checked).
  */
 #ifndef KMEANS_MI355X_H
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define KMEANS_ABI_VERSION 2
+#define KMEANS_ABI_VERSION 3
 
 /* Supported feature dimension: 16 <= D <= 512 and D % 16 == 0. */
 #define KMEANS_MIN_D 16
@@ -144,6 +145,44 @@ kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_uni
                             int32_t *path, int32_t *splits, int32_t *workgroups,
                             int32_t *points_per_wg, int32_t *k_block,
                             int32_t *padded_d);
+
+/*
+ * Centroid update: the step that follows assignment in a Lloyd (k-means)
+ * iteration.  The pages describe the assignment step only (Summary); this
+ * is the plain definition of the update, with the readings noted:
+ *
+ *     counts[k] = #{ i : labels[i] == k }
+ *     means[k]  = (sum of x_i over those i) / counts[k]      (fp32)
+ *     C_new[k]  = means[k] rounded to bf16 (nearest, ties to even), or
+ *                 C_old[k] bit for bit when counts[k] == 0 (empty cluster)
+ *     norms[k]  = ||C_new[k]||^2, the same bits kmeans_centroid_norms gives
+ *                 for C_new (so C_new and norms feed kmeans_assign directly)
+ *
+ *   X       bf16 [N][D] points, row-major, 16-byte aligned.
+ *   labels  int32 [N], 4-byte aligned; a label outside [0, K) counts for no
+ *           cluster (X and labels may be NULL when N == 0).
+ *   C_old   bf16 [K][D] current centroids, 16-byte aligned; read only for
+ *           empty clusters.  C_new may be C_old itself (an in-place update);
+ *           no other overlap between inputs and outputs is allowed.
+ *   N       0 <= N < 2^31 (N == 0: every cluster is empty).
+ *   D       16 <= D <= 512, D % 16 == 0.
+ *   K       1 <= K < 2^31.
+ *   C_new   bf16 [K][D], 16-byte aligned, written.
+ *   norms   fp32 [K], written.  counts int32 [K], written.
+ *   means   fp32 [K][D] or NULL (then not written); an empty cluster's row
+ *           is its old centroid widened to fp32.
+ *
+ * The sums are fp32, each in an order fixed by the data (points grouped by
+ * label in index order, in chunks of 128 sorted positions whose partial sums
+ * add in chunk order), so the outputs are bitwise deterministic; IEEE
+ * arithmetic throughout (a NaN coordinate makes that coordinate of the mean
+ * NaN).  Scratch of about 16 bytes per point plus 8 bytes per cluster comes
+ * from hipMallocAsync/hipFreeAsync on `stream`; KMEANS_ERR_NO_MEMORY if it
+ * fails.
+ */
+kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
+                              int64_t N, int64_t D, int64_t K, void *C_new, float *norms,
+                              int32_t *counts, float *means, hipStream_t stream);
 
 /* Thread-local message for the last non-OK status ("" if none). */
 const char *kmeans_last_error(void);

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) k-means assignment: Python binding of ``libkmeans_mi355x.so``.
+"""MI355X (gfx950) k-means assignment and centroid update: Python binding of
+``libkmeans_mi355x.so``.
 
 The functions here only marshal torch tensors into the C ABI declared in
 ``include/kmeans_mi355x.h`` (device pointers, sizes, the current HIP stream);
@@ -7,6 +8,7 @@ CPU fallback: if the library is missing, the first call raises.
 
     norms = kmeans_centroid_norms(C)                    # fp32 [K]
     labels, min_dist = kmeans_assign(X, C, norms)       # int32 [N], fp32 [N]
+    C, norms, counts, _ = kmeans_update(X, labels, C)   # next Lloyd iterate
 
 ``X`` and ``C`` are ``torch.bfloat16`` CUDA tensors of shape ``[N, D]`` and
 ``[K, D]``, contiguous.  Calls are asynchronous on the current stream.
@@ -72,6 +74,8 @@ def load_library(path: str = LIBRARY):
     lib.kmeans_assign_path.restype = ctypes.c_int
     lib.kmeans_plan.argtypes = [i64, i64, i64, i32, i32p, i32p, i32p, i32p, i32p, i32p]
     lib.kmeans_plan.restype = ctypes.c_int
+    lib.kmeans_update.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.kmeans_update.restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
     lib.kmeans_last_error.restype = ctypes.c_char_p
     lib.kmeans_abi_version.argtypes = []
@@ -171,6 +175,47 @@ def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, count: int = 0,
     _check(lib, lib.kmeans_assign_path(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
                                        _ptr(min_dist), path, count, _stream_handle(stream)))
     return labels, min_dist
+
+
+def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=None,
+                  with_means: bool = False, stream=None):
+    """Centroid update from ``labels``: ``(C_new bf16 [K, D], norms fp32 [K],
+    counts int32 [K], means fp32 [K, D] or None)``.  An empty cluster keeps
+    its row of ``C_old``; labels outside ``[0, K)`` count for no cluster.
+    ``C_new`` may be ``C_old`` itself (in-place update)."""
+    import torch
+    X = _matrix(X, "X")
+    C_old = _matrix(C_old, "C_old")
+    N, D = X.shape
+    K = C_old.shape[0]
+    if C_old.shape[1] != D:
+        raise ValueError(f"X has D={D} but C_old has D={C_old.shape[1]}")
+    if (not isinstance(labels, torch.Tensor) or labels.dtype != torch.int32
+            or not labels.is_cuda or labels.numel() != N or not labels.is_contiguous()):
+        raise ValueError("labels must be a contiguous int32 CUDA tensor of N elements")
+    dev = C_old.device
+    if C_new is None:
+        C_new = torch.empty_like(C_old)
+    else:
+        C_new = _matrix(C_new, "C_new")
+        if C_new.shape != C_old.shape:
+            raise ValueError("C_new must have the shape of C_old")
+    if norms is None:
+        norms = torch.empty(K, dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(K, dtype=torch.int32, device=dev)
+    if means is None and with_means:
+        means = torch.empty((K, D), dtype=torch.float32, device=dev)
+    for t, name, dt, n in ((norms, "norms", torch.float32, K), (counts, "counts", torch.int32, K),
+                           (means, "means", torch.float32, K * D)):
+        if t is not None and (t.dtype != dt or not t.is_cuda or t.numel() != n
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor of {n} elements")
+    lib = load_library()
+    _check(lib, lib.kmeans_update(_ptr(X), _ptr(labels), _ptr(C_old), N, D, K, _ptr(C_new),
+                                  _ptr(norms), _ptr(counts), _ptr(means),
+                                  _stream_handle(stream)))
+    return C_new, norms, counts, means
 
 
 def assign(X, C, norms=None):

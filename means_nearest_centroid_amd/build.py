@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libkmeans_mi355x.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("kmeans_kernels.hip", "kmeans_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kmeans_kernels.hip", "kmeans_update.hip",
+                                           "kmeans_api.hip")]
 PROBE_LIBRARY = os.path.join(PKG, "libkmeans_mfma_stream.so")
 PROBE_SOURCES = [os.path.join(CSRC, "mfma_stream.hip")]
 ARCH = "gfx950"

@@ -76,6 +76,59 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
 
 hipError_t launch_norms(const uint16_t *C, int K, int D, float *norms, hipStream_t stream);
 
+// Squared norm of one bf16 row of D values (D % 8 == 0) as a group of 16
+// lanes computes it: lane l fma-accumulates the 16-byte chunks l, l + 16, ...
+// (low, then high half of each 32-bit word), and the 16 partial sums combine
+// over an xor tree, so every lane of the group returns the same value.  The
+// norms pre-pass and the centroid update both use it, so a row gets the same
+// norm bits from either.  Every lane of the wave must call it (the xor tree
+// reads all 16 lanes of each group); a lane with nothing to add passes D = 0.
+__device__ __forceinline__ float row_sq_norm16(const uint16_t *row, int D, int l) {
+    typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+    float acc = 0.0f;
+    for (int c = l; c * 8 < D; c += 16) {
+        const w4 v = *reinterpret_cast<const w4 *>(row + c * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float lo = __uint_as_float(v[w] << 16);
+            const float hi = __uint_as_float(v[w] & 0xffff0000u);
+            acc = fmaf(lo, lo, acc);
+            acc = fmaf(hi, hi, acc);
+        }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+        acc += __shfl_xor(acc, m, 16);
+    return acc;
+}
+
+// ---- centroid update (the step after assignment in a Lloyd iteration) ----
+
+// Workspace layout and launch shape of one kmeans_update call.
+struct UpdatePlan {
+    int passes;        // 8-bit radix passes over the keys 0..K (K = stray label)
+    int tile_log2;     // sort tile of 2^tile_log2 points (>= 1024)
+    int tiles;         // sort tiles
+    int chunks;        // reduce chunks of kUpdateChunk sorted positions
+    size_t keys[2], vals[2];   // byte offsets of the ping-pong sort buffers
+    size_t hist;       // [passes][256][tiles] int32
+    size_t start, end; // [K] int32 each
+    size_t partial;    // [chunks][2][D] fp32
+    size_t bytes;      // total workspace (0 when N == 0)
+};
+
+constexpr int kUpdateChunk = 128;   // sorted positions per reduce wave
+
+// Requires 0 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller).
+UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K);
+
+// All launches of one update on `stream`; ws holds plan.bytes bytes (may be
+// null when N == 0).  means may be null.
+hipError_t launch_update(const UpdatePlan &plan, const uint16_t *X, const int32_t *labels,
+                         const uint16_t *C_old, int N, int D, int K, uint16_t *C_new,
+                         float *norms, int32_t *counts, float *means, void *ws,
+                         hipStream_t stream);
+
 // Direct path when ws_score == nullptr, otherwise writes per-split partial
 // winners to the workspace and the merge kernel finishes.
 hipError_t launch_assign(const Plan &plan, const uint16_t *X, const uint16_t *C,

@@ -495,25 +495,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void norms_kernel(const uint16_t *__restrict__ C, int K, int D, float *__restrict__ norms) {
     const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
     const int l = threadIdx.x & 15;
-    float acc = 0.0f;
-    if (row < K) {
-        const uint16_t *cr = C + static_cast<size_t>(row) * D;
-        for (int c = l; c * 8 < D; c += 16) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(cr + c * 8);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float lo = __uint_as_float(v[w] << 16);
-                const float hi = __uint_as_float(v[w] & 0xffff0000u);
-                acc = fmaf(lo, lo, acc);
-                acc = fmaf(hi, hi, acc);
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
-        acc += __shfl_xor(acc, m, 16);
-    if (row < K && l == 0)
-        norms[row] = acc;
+    const bool live = row < K;
+    const float n = row_sq_norm16(C + static_cast<size_t>(live ? row : 0) * D, live ? D : 0, l);
+    if (live && l == 0)
+        norms[row] = n;
 }
 
 template <int KS, int P>

@@ -94,3 +94,108 @@ def sample_indices(N: int, seed: int = 0, head: int = 2048, rand: int = 2048, ta
     parts = [np.arange(min(head, N)), rng.integers(0, N, size=min(rand, N)),
              np.arange(max(0, N - tail), N)]
     return np.unique(np.concatenate(parts))
+
+
+# ---------------------------------------------------------------------------
+# Centroid update
+# ---------------------------------------------------------------------------
+#
+# For a cluster of n points with exact mean m (the oracle's fp64 mean: bf16
+# sums of this size are exact in fp64) and S = sum of |x_ij| over its
+# points, any fp32 summation order is within (n - 1) u S of the exact sum
+# (u = 2^-24; the bound of recursive and of any tree summation), and the
+# division adds u |m|.  So a GPU mean must satisfy
+#
+#     |mean_gpu - m| <= tol = 1.01 u ((n - 1) S / n + |m|) + 2^-149,
+#
+# and its bf16 row, the rounding of some value within tol of m, must lie
+# between rne(m - tol) and rne(m + tol) (rounding is monotone).  Counts are
+# exact; an empty cluster's row is the old row bit for bit; non-finite means
+# match in class.
+
+U32 = 2.0 ** -24
+
+
+def _members_abs_sum(X, labels, K):
+    """Per cluster and coordinate, the sum of |x_ij| over its points (fp32
+    accumulation: this only sizes the tolerance)."""
+    S = np.zeros((K, X.shape[1]))
+    idx = np.flatnonzero((labels >= 0) & (labels < K))
+    if len(idx) == 0:
+        return S
+    idx = idx[np.argsort(labels[idx], kind="stable")]
+    lab = labels[idx]
+    Xa = np.abs((X[idx].astype(np.uint32) << 16).view(np.float32))
+    first, starts = np.unique(lab, return_index=True)
+    S[first] = np.add.reduceat(Xa, starts, axis=0)
+    return S
+
+
+def _widen(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_update(X, labels, C_old, C_new, norms, counts, means=None, ref=None):
+    """Check a GPU centroid update (numpy arrays) against the oracle."""
+    labels = np.asarray(labels, dtype=np.int32)
+    C_new = np.asarray(C_new, dtype=np.uint16)
+    K, D = C_old.shape
+    if ref is None:
+        ref = oracle.update(X, labels, C_old)
+    problems = []
+    if not np.array_equal(np.asarray(counts, dtype=np.int64), ref["counts"]):
+        bad = np.flatnonzero(np.asarray(counts) != ref["counts"])[:5]
+        problems.append(f"counts differ at {bad}: gpu={np.asarray(counts)[bad]} "
+                        f"oracle={ref['counts'][bad]}")
+    empty = ref["counts"] == 0
+    if not np.array_equal(C_new[empty], C_old[empty]):
+        problems.append("an empty cluster's row changed")
+    m = ref["means"]
+    n = np.maximum(ref["counts"], 1).astype(np.float64)[:, None]
+    S = _members_abs_sum(X, labels, K)
+    with np.errstate(invalid="ignore", over="ignore"):
+        tol = 1.01 * U32 * ((n - 1.0) / n * S + np.abs(m)) + 2.0 ** -149
+        lo = _widen(oracle.bf16_from_double(m - tol))
+        hi = _widen(oracle.bf16_from_double(m + tol))
+    got = _widen(C_new)
+    fin = np.isfinite(m) & ~empty[:, None]
+    with np.errstate(invalid="ignore"):
+        bad_row = fin & ~((got >= lo) & (got <= hi))
+    nonfin = ~np.isfinite(m) & ~empty[:, None]
+    bad_cls = nonfin & ~((np.isnan(m) & np.isnan(got)) | (np.isinf(m) & (got == m)))
+    if bad_row.any():
+        k, j = np.argwhere(bad_row)[0]
+        problems.append(f"{int(bad_row.sum())} bf16 elements out of bounds, first [{k},{j}]: "
+                        f"gpu={got[k, j]!r} oracle mean={m[k, j]!r} tol={tol[k, j]!r}")
+    if bad_cls.any():
+        k, j = np.argwhere(bad_cls)[0]
+        problems.append(f"non-finite class mismatch at [{k},{j}]: gpu={got[k, j]!r} "
+                        f"oracle={m[k, j]!r}")
+    if means is not None:
+        mg = np.asarray(means, dtype=np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            bad_m = fin & ~(np.abs(mg - m) <= tol)
+        if not np.array_equal(mg[empty], _widen(C_old[empty])):
+            problems.append("an empty cluster's fp32 mean is not its old row")
+        if bad_m.any():
+            k, j = np.argwhere(bad_m)[0]
+            problems.append(f"{int(bad_m.sum())} fp32 means out of bounds, first [{k},{j}]: "
+                            f"gpu={mg[k, j]!r} oracle={m[k, j]!r} tol={tol[k, j]!r}")
+        # the bf16 row is the rounding of the fp32 mean the GPU computed
+        if not np.array_equal(oracle.bf16_from_double(mg)[~empty], C_new[~empty]):
+            problems.append("bf16 row is not the rounding of the fp32 mean")
+    # norms: a property of whatever rows came out
+    cn = _widen(C_new)
+    with np.errstate(invalid="ignore", over="ignore"):
+        nn = (cn * cn).sum(1)
+        g = np.asarray(norms, dtype=np.float64)
+        okn = np.isfinite(nn)
+        bad_n = okn & ~(np.abs(g - nn) <= 2e-6 * nn + 1e-30)
+    if bad_n.any():
+        k = np.flatnonzero(bad_n)[0]
+        problems.append(f"norm of row {k}: gpu={g[k]!r} sum of squares={nn[k]!r}")
+    if problems:
+        raise AssertionError("update parity failure:\n" + "\n".join(problems))
+    return dict(clusters=K, empty=int(empty.sum()),
+                exact=int((got[fin] == _widen(oracle.bf16_from_double(m))[fin]).sum()),
+                elements=int(fin.sum()))

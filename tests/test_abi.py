@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("kmeans_centroid_norms", "kmeans_assign", "kmeans_assign_path",
-              "kmeans_plan", "kmeans_last_error", "kmeans_abi_version"):
+              "kmeans_plan", "kmeans_update", "kmeans_last_error", "kmeans_abi_version"):
         assert f in names
 
 
@@ -204,3 +204,33 @@ def test_plan_rejects_bad_shapes(lib):
         km.kmeans_plan(10, 72, 5)
     with pytest.raises(km.KmeansError):
         km.kmeans_plan(10, 64, 0)
+
+
+def update_status(lib, X=FAKE, lab=FAKE, C=FAKE, N=10, D=64, K=5, Cn=FAKE, n=FAKE, cnt=FAKE,
+                  m=NUL):
+    return lib.kmeans_update(X, lab, C, N, D, K, Cn, n, cnt, m, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), km.KMEANS_ERR_INVALID_ARG),
+    (dict(K=0), km.KMEANS_ERR_INVALID_ARG),
+    (dict(D=40), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(D=1024), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(N=1 << 31), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(K=1 << 31), km.KMEANS_ERR_UNSUPPORTED),
+    (dict(X=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(lab=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(C=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(Cn=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(n=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(cnt=NUL), km.KMEANS_ERR_INVALID_ARG),
+    (dict(N=0, C=NUL), km.KMEANS_ERR_INVALID_ARG),    # outputs are written even at N = 0
+    (dict(X=FAKE_ODD), km.KMEANS_ERR_ALIGNMENT),
+    (dict(C=FAKE_ODD), km.KMEANS_ERR_ALIGNMENT),
+    (dict(Cn=FAKE_ODD), km.KMEANS_ERR_ALIGNMENT),
+    (dict(lab=ctypes.c_void_p(0x10001)), km.KMEANS_ERR_ALIGNMENT),
+    (dict(m=ctypes.c_void_p(0x10001)), km.KMEANS_ERR_ALIGNMENT),
+])
+def test_update_rejects_bad_arguments(lib, kw, status):
+    assert update_status(lib, **kw) == status
+    assert lib.kmeans_last_error().decode()

@@ -88,3 +88,85 @@ def test_out_of_range_label_fails(case):
     lab[7] = C.shape[0]
     with pytest.raises(AssertionError, match="out of range"):
         parity.check(X, C, lab, md, ref=ref)
+
+
+# ---- centroid update rule -------------------------------------------------
+
+@pytest.fixture(scope="module")
+def upd_case():
+    X, C, a = W.gaussian_mixture(4000, 64, 200, 61)
+    lab = a.astype(np.int32)
+    lab[:40] = -1
+    lab[lab == 9] = 10                     # cluster 9 empty
+    ref = oracle.update(X, lab, C)
+    return X, C, lab, ref
+
+
+def upd_outputs(C, ref):
+    """The oracle's result written as a GPU would return it."""
+    m32 = ref["means"].astype(np.float32)
+    Cn = oracle.bf16_from_double(m32.astype(np.float64))
+    empty = ref["counts"] == 0
+    Cn[empty] = C[empty]
+    nn = (parity._widen(Cn) ** 2).sum(1).astype(np.float32)
+    return Cn, nn, ref["counts"].astype(np.int32), m32
+
+
+def test_update_oracle_outputs_pass(upd_case):
+    X, C, lab, ref = upd_case
+    st = parity.check_update(X, lab, C, *upd_outputs(C, ref), ref=ref)
+    assert st["empty"] == 1 and st["exact"] > 0.99 * st["elements"]
+
+
+def test_update_wrong_count_fails(upd_case):
+    X, C, lab, ref = upd_case
+    Cn, nn, cnt, m = upd_outputs(C, ref)
+    cnt[3] += 1
+    with pytest.raises(AssertionError, match="counts differ"):
+        parity.check_update(X, lab, C, Cn, nn, cnt, m, ref=ref)
+
+
+def test_update_empty_row_must_be_kept(upd_case):
+    X, C, lab, ref = upd_case
+    Cn, nn, cnt, m = upd_outputs(C, ref)
+    Cn[9, 0] ^= 1
+    with pytest.raises(AssertionError, match="empty cluster's row"):
+        parity.check_update(X, lab, C, Cn, nn, cnt, ref=ref)
+
+
+def test_update_dropped_point_fails(upd_case):
+    X, C, lab, ref = upd_case
+    Cn, nn, cnt, m = upd_outputs(C, ref)
+    k = int(lab[100])
+    members = np.flatnonzero(lab == k)
+    xs = parity._widen(X[members[1:]])                 # one point left out
+    m[k] = (xs.sum(0) / len(members)).astype(np.float32)
+    with pytest.raises(AssertionError, match="fp32 means out of bounds"):
+        parity.check_update(X, lab, C, Cn, nn, cnt, m, ref=ref)
+
+
+def test_update_bf16_off_by_one_ulp_fails(upd_case):
+    X, C, lab, ref = upd_case
+    Cn, nn, cnt, m = upd_outputs(C, ref)
+    Cn[5, 7] += 1                                      # next bf16 up
+    with pytest.raises(AssertionError, match="bf16 elements out of bounds"):
+        parity.check_update(X, lab, C, Cn, nn, cnt, ref=ref)
+
+
+def test_update_row_must_round_its_mean(upd_case):
+    X, C, lab, ref = upd_case
+    Cn, nn, cnt, m = upd_outputs(C, ref)
+    m[5, 7] = np.nextafter(m[5, 7], np.float32(np.inf))   # within tol, row unchanged
+    parity.check_update(X, lab, C, Cn, nn, cnt, m, ref=ref)
+    k, j = 6, 3
+    Cn[k, j] = Cn[k, j] + 1 if parity._widen(Cn[k, j]) > 0 else Cn[k, j] - 1
+    with pytest.raises(AssertionError, match="bf16"):
+        parity.check_update(X, lab, C, Cn, nn, cnt, m, ref=ref)
+
+
+def test_update_wrong_norm_fails(upd_case):
+    X, C, lab, ref = upd_case
+    Cn, nn, cnt, m = upd_outputs(C, ref)
+    nn[4] *= np.float32(1.001)
+    with pytest.raises(AssertionError, match="norm of row 4"):
+        parity.check_update(X, lab, C, Cn, nn, cnt, m, ref=ref)

@@ -40,32 +40,53 @@ BF16_DENSE_PEAK_TFLOPS = 2516.6     # MI355X: 256 CU x 4096 flop/clk x 2.4 GHz
 KERNEL_SOURCES = ("means_nearest_centroid_amd/csrc/kmeans_kernels.hip",
                   "means_nearest_centroid_amd/csrc/kmeans_internal.h",
                   "means_nearest_centroid_amd/csrc/kmeans_api.hip")
+UPDATE_SOURCES = KERNEL_SOURCES + ("means_nearest_centroid_amd/csrc/kmeans_update.hip",)
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_record(config: int):
-    """HBM bytes per assign launch from the committed counter summary, if it
-    was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_assign_workload{config}.json")
+def _traffic_path(config: int, kind: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{kind}_workload{config}.json")
+
+
+def traffic_record(config: int, kind: str = "assign"):
+    """HBM bytes per assign launch (or per update call) from the committed
+    counter summary, if it was taken on the current kernel sources; else None."""
+    path = _traffic_path(config, kind)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    sources = UPDATE_SOURCES if kind == "update" else KERNEL_SOURCES
+    if rec.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return rec
 
 
+def _kernel_kind(name: str):
+    if "assign_kernel" in name:
+        return "assign"
+    if "merge_kernel" in name:
+        return "merge"
+    if "neg_kernel" in name:
+        return "copy"
+    if "upd_" in name:
+        return "update"
+    return None
+
+
 def _counter_per_dispatch(csv_path: str, counter: str):
-    """Mean per-dispatch value of `counter` for the assign kernel and for the
-    calibration copy kernel, from a rocprofv3 --pmc counter_collection.csv."""
+    """Per kernel kind (assign, merge, calibration copy, and the update's
+    kernels together), the counter's total over all dispatches and the number
+    of dispatches, from a rocprofv3 --pmc counter_collection.csv; for the
+    update, the dispatches of its finish kernel (one per call)."""
     import csv
     import collections
     tot = collections.defaultdict(float)
@@ -75,30 +96,37 @@ def _counter_per_dispatch(csv_path: str, counter: str):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            kind = "assign" if "assign_kernel" in name else (
-                "merge" if "merge_kernel" in name else (
-                    "copy" if "neg_kernel" in name else None))
+            kind = _kernel_kind(name)
             if kind is None:
                 continue
             tot[kind] += float(row["Counter_Value"])
-            disp[kind].add(row["Dispatch_Id"])
+            if kind != "update" or "upd_finish_kernel" in name:
+                disp[kind].add(row["Dispatch_Id"])
     return {k: tot[k] / len(disp[k]) for k in tot}
 
 
-def record_traffic(config: int, fetch_csv: str, write_csv: str, copy_mib: int, command: str):
+def record_traffic(config: int, fetch_csv: str, write_csv: str, copy_mib: int, command: str,
+                   kind: str = "assign"):
     """Write the HBM-traffic record bench.py reports: counter KiB per assign
-    launch, scaled by what the same counter reads for a plain copy of known
-    size (copy_mib MiB read and written)."""
+    launch (or per update call, all its kernels), scaled by what the same
+    counter reads for a plain copy of known size (copy_mib MiB read and
+    written)."""
     fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
     known = copy_mib * 1024.0                       # KiB read, and written, by the copy
     f_scale = known / fetch["copy"]
     w_scale = known / write["copy"]
-    kib_assign = fetch["assign"] + fetch.get("merge", 0.0)
-    kib_assign_w = write["assign"] + write.get("merge", 0.0)
+    if kind == "update":
+        kib_assign = fetch["update"]
+        kib_assign_w = write["update"]
+    else:
+        kib_assign = fetch["assign"] + fetch.get("merge", 0.0)
+        kib_assign_w = write["assign"] + write.get("merge", 0.0)
     rec = dict(
         workload=config,
-        kernel_source_hash=kernel_source_hash(),
+        step=kind,
+        kernel_source_hash=kernel_source_hash(UPDATE_SOURCES if kind == "update"
+                                              else KERNEL_SOURCES),
         fetch_kib_per_launch=kib_assign,
         write_kib_per_launch=kib_assign_w,
         copy_fetch_kib=fetch["copy"], copy_write_kib=write["copy"], copy_kib=known,
@@ -106,7 +134,7 @@ def record_traffic(config: int, fetch_csv: str, write_csv: str, copy_mib: int, c
         hbm_bytes_per_launch=int(round((kib_assign * f_scale + kib_assign_w * w_scale) * 1024)),
         command=command,
     )
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_assign_workload{config}.json")
+    path = _traffic_path(config, kind)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -282,6 +310,120 @@ def cpu_baseline(X, C, target_s: float):
                        f"centroids, fp64, {dt:.2f} s wall")
 
 
+UPDATE_METRIC = "centroid update (Lloyd step after assignment): points/sec at N={N},D={D},K={K} (1 GPU)"
+
+
+def update_bytes(N: int, D: int, K: int) -> int:
+    """Algorithmic HBM bytes of one update call without the fp32 means: every
+    point row and label read once, every new row, norm and count written once
+    (old rows are read only for empty clusters, none here)."""
+    return N * (2 * D + 4) + K * (2 * D + 8)
+
+
+def run_update(args):
+    """Time kmeans_update (the Lloyd step after assignment) on one workload:
+    three seeded sets resident and rotated, labels = each point's generating
+    centre, outputs preallocated, no fp32 means.  One JSON line."""
+    import torch
+    import means_nearest_centroid_amd as km
+
+    cfg = W.CONFIGS[args.config]
+    N, D, K = cfg["N"], cfg["D"], cfg["K"]
+    print(f"[bench] update: generating workload {args.config} ({cfg['name']})",
+          file=sys.stderr, flush=True)
+    host = []
+    for s in W.SEEDS:
+        X, C, meta = W.make_config(args.config, s)
+        host.append((X, C, np.ascontiguousarray(meta["generating_centre"], dtype=np.int32)))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    km.load_library()
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sets = [(to_dev(X), torch.from_numpy(lab).to(dev), to_dev(C)) for X, C, lab in host]
+    C_new = torch.empty((K, D), dtype=torch.bfloat16, device=dev)
+    norms = torch.empty(K, dtype=torch.float32, device=dev)
+    counts = torch.empty(K, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        X, lab, C = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        km.kmeans_update(X, lab, C, C_new, norms, counts, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    settled = settle(step, args.settle_ms)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    call_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+
+    nbytes = update_bytes(N, D, K)
+    avg_s = float(call_ms.mean()) / 1e3
+    achieved = nbytes / avg_s / 1e9
+    traffic = traffic_record(args.config, "update")
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        X0, C0, l0 = host[0]
+        t0 = time.perf_counter()
+        oracle.update(X0, l0, C0)
+        dt = time.perf_counter() - t0
+        cpu = dict(value=N / dt, unit="points/s", cores=1, kind="oracle",
+                   sample=f"the whole workload (seed {W.SEEDS[0]}), fp64, one thread, "
+                          f"{dt:.2f} s wall")
+    out = {
+        "metric": UPDATE_METRIC.format(N=N, D=D, K=K),
+        "value": N / (ms_per_step / 1e3),
+        "unit": "points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"centroid update, {cfg['name']}, bf16 Gaussian mixture, labels "
+                               f"= generating centres, seeds {list(W.SEEDS)} rotated",
+                   "N": N, "D": D, "K": K, "settle_ms": args.settle_ms,
+                   "settle_steps": settled},
+        "roofline": dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                         unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                         traffic=(traffic["hbm_bytes_per_launch"] if traffic else None),
+                         kernel="kmeans_update (all its kernels, one call)",
+                         avg_launch_us=round(avg_s * 1e6, 2), bytes_per_launch=nbytes),
+        "cpu_baseline": cpu,
+        "breakdown_us": {"call_median": round(float(np.median(call_ms)) * 1e3, 2),
+                         "call_min": round(float(call_ms.min()) * 1e3, 2),
+                         "call_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +444,9 @@ def main():
     ap.add_argument("--record-command", default="", help="command stored with the record")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the MFMA-only probe (mfma_ceiling: null)")
+    ap.add_argument("--update", action="store_true",
+                    help="time kmeans_update (the Lloyd step after assignment) on the "
+                         "workload instead (one JSON line)")
     ap.add_argument("--sweep", action="store_true",
                     help="time kmeans_assign on the pages' 13 shapes instead (one JSON "
                          "line per shape)")
@@ -309,7 +454,8 @@ def main():
 
     if args.record_traffic:
         record_traffic(args.config, args.record_traffic[0], args.record_traffic[1],
-                       args.copy_calibration_mib or 256, args.record_command)
+                       args.copy_calibration_mib or 256, args.record_command,
+                       kind="update" if args.update else "assign")
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -319,6 +465,9 @@ def main():
 
     if args.sweep:
         run_sweep(args)
+        return
+    if args.update:
+        run_update(args)
         return
 
     import torch

@@ -109,15 +109,15 @@ struct UpdatePlan {
     int passes;        // 8-bit radix passes over the keys 0..K (K = stray label)
     int tile_log2;     // sort tile of 2^tile_log2 points (>= 1024)
     int tiles;         // sort tiles
-    int chunks;        // reduce chunks of kUpdateChunk sorted positions
+    int stride;        // histogram row length: tiles rounded up to 4
+    int chunk;         // sorted positions per reduce chunk (64 KiB of rows, <= 1024)
+    int chunks;        // reduce chunks
     size_t keys[2], vals[2];   // byte offsets of the ping-pong sort buffers
-    size_t hist;       // [passes][256][tiles] int32
+    size_t hist;       // [passes][256][stride] int32
     size_t start, end; // [K] int32 each
     size_t partial;    // [chunks][2][D] fp32
     size_t bytes;      // total workspace (0 when N == 0)
 };
-
-constexpr int kUpdateChunk = 128;   // sorted positions per reduce wave
 
 // Requires 0 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller).
 UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K);

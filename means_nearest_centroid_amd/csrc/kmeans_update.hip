@@ -16,20 +16,22 @@
 //  1. Points are grouped by label with a stable LSD radix sort of the keys
 //     (label, or K for a stray label) carrying the point index, on 8-bit
 //     digits.  A pass is: a per-tile digit histogram, one exclusive scan over
-//     (digit, tile), and a scatter in which every tile ranks its keys in
-//     index order -- wave ballots give the rank among equal digits inside a
-//     wave, and a per-wave count table in LDS, tagged with the round so it
-//     never needs clearing, the rank across the tile's waves.  The scatter of
-//     one pass also counts the next pass's digits per destination tile
-//     (integer atomics), so only the first pass has a histogram kernel.
-//  2. The reduce kernel gives each wave a fixed chunk of sorted positions.  A
-//     wave walks its chunk in order, gathering one row per position (all 64
-//     lanes share the row, V bf16 values each) and adding it to the running
-//     sum of the current run of equal labels.  A cluster that starts and ends
-//     inside the chunk is finished there; a run cut by a chunk boundary
-//     leaves its partial sum, and the finish kernel adds a cluster's partials
-//     in chunk order.  Work per wave is bounded by the chunk, whatever the
-//     cluster sizes, and the order of every sum is fixed by the sorted order.
+//     (digit, tile) -- done by every scatter workgroup for its own tile when
+//     there are at most 128 tiles, by a scan kernel beyond -- and a scatter
+//     in which every tile ranks its keys in index order: wave ballots give
+//     the rank among equal digits inside a wave, and a per-wave count table
+//     in LDS, tagged with the round so it never needs clearing, the rank
+//     across the tile's waves.
+//  2. The reduce kernel gives each workgroup a fixed chunk of sorted
+//     positions (32 KiB of rows: 128 at D = 128).  It first stages the
+//     chunk's rows in LDS with all row loads in flight at once (a gather of
+//     whole rows, 16 bytes per load), then its waves sum each run of equal
+//     labels from LDS in position order (64 lanes share a row, V bf16 values
+//     each).  A cluster that starts and ends inside the chunk is finished
+//     there; a run cut by a chunk boundary leaves its partial sum, and the
+//     finish kernel adds a cluster's partials in chunk order.  Work per
+//     workgroup is bounded by the chunk, whatever the cluster sizes, and the
+//     order of every sum is fixed by the sorted order.
 //  3. Finishing a cluster: mean = sum / count in fp32, rounded to bf16, and
 //     the squared norm of the rounded row computed exactly as the norms
 //     pre-pass computes it (row_sq_norm16 over a copy of the row in LDS).
@@ -43,9 +45,16 @@ namespace {
 constexpr int kSortThreads = 256;    // 4 waves; one key per thread per round
 constexpr int kRadix = 256;
 constexpr int kScanThreads = 1024;
-constexpr int kReduceWaves = 4;
-constexpr int kPrefetch = 16;        // rows in flight per wave in the reduce
+constexpr int kFusedScanTiles = 128;  // up to this many sort tiles, no scan kernel
+constexpr int kScatterThreads = 1024; // 16 waves: 1024 keys per scatter round
+constexpr int kBatchRounds = 4;       // scatter rounds whose keys load together
+constexpr int kReduceThreads = 256;  // 4 waves
 constexpr int kMaxRow = 512;         // bf16 values of the widest supported row
+// Rows of one reduce chunk staged in LDS: 32 KiB, so four workgroups share
+// a CU (1024 at once on 256 CUs); 8 loads of 16 bytes per thread fill it.
+constexpr int kStageBytes = 32768;
+constexpr int kStagePieces = kStageBytes / 16 / kReduceThreads;
+constexpr int kMaxChunk = 480;        // keeps a reduce workgroup within 40 KiB of LDS
 
 __device__ __forceinline__ int sort_key(int32_t label, int K) {
     return (label < 0 || label >= K) ? K : label;
@@ -65,13 +74,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 // ---- 1. radix sort -------------------------------------------------------
 
-// Pass-0 digit histogram of one tile, written digit-major ([digit][tile]).
-// The same launch clears the cluster bounds and the histograms the later
-// passes accumulate into.
+// Digit histogram of one tile for the pass on (key >> shift) & 255, written
+// digit-major ([digit][tile]).  FIRST: keys come from the labels, and the
+// launch also clears the cluster bounds (clear, n_clear entries).
+template <bool FIRST>
 __global__ __launch_bounds__(kSortThreads)
-void upd_hist_kernel(const int32_t *__restrict__ labels, int N, int K, int tile_log2, int tiles,
-                     int32_t *__restrict__ hist0, int32_t *__restrict__ clear_a, int64_t n_a,
-                     int32_t *__restrict__ clear_b, int64_t n_b) {
+void upd_hist_kernel(const int32_t *__restrict__ keys_in, int N, int K, int shift, int tile_log2,
+                     int tiles, int stride, int32_t *__restrict__ hist, int32_t *__restrict__ clear,
+                     int64_t n_clear) {
     __shared__ int h[kRadix];
     const int tid = threadIdx.x;
     h[tid] = 0;
@@ -80,111 +90,236 @@ void upd_hist_kernel(const int32_t *__restrict__ labels, int N, int K, int tile_
     const int beg = t << tile_log2;
     const int fin = static_cast<int>(min(static_cast<int64_t>(N),
                                          static_cast<int64_t>(beg) + (int64_t(1) << tile_log2)));
-    for (int i = beg + tid; i < fin; i += kSortThreads)
-        atomicAdd(&h[sort_key(labels[i], K) & (kRadix - 1)], 1);
+    for (int i = beg + tid; i < fin; i += kSortThreads) {
+        const int key = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
+        atomicAdd(&h[(key >> shift) & (kRadix - 1)], 1);
+    }
     __syncthreads();
-    hist0[static_cast<size_t>(tid) * tiles + t] = h[tid];
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kSortThreads;
-    for (int64_t j = static_cast<int64_t>(t) * kSortThreads + tid; j < n_a; j += stride)
-        clear_a[j] = 0;
-    for (int64_t j = static_cast<int64_t>(t) * kSortThreads + tid; j < n_b; j += stride)
-        clear_b[j] = 0;
+    int32_t *row = hist + static_cast<size_t>(tid) * stride;
+    row[t] = h[tid];
+    if (t == tiles - 1)                    // rows are padded to a multiple of 4
+        for (int p = tiles; p < stride; ++p)
+            row[p] = 0;
+    if (FIRST) {
+        const int64_t step = static_cast<int64_t>(gridDim.x) * kSortThreads;
+        for (int64_t j = static_cast<int64_t>(t) * kSortThreads + tid; j < n_clear; j += step)
+            clear[j] = 0;
+    }
 }
 
-// Exclusive scan of h[0..M) in place, one workgroup: each thread owns a
-// contiguous run of entries.
+// Exclusive scan of h[0..M) in place (M a multiple of 4), one workgroup:
+// each thread owns a contiguous run of 16-byte groups, loaded eight at a
+// time into registers so the loads overlap (one batch when M <= 32768, and
+// then the values stay in registers for the write-back).
 __global__ __launch_bounds__(kScanThreads)
 void upd_scan_kernel(int32_t *__restrict__ h, int M) {
-    __shared__ int part[kScanThreads];
+    typedef int32_t i4 __attribute__((ext_vector_type(4)));
+    constexpr int kBatch = 8;
+    __shared__ int wtot[kScanThreads / 64];
     const int tid = threadIdx.x;
-    const int per = (M + kScanThreads - 1) / kScanThreads;
-    const int b = min(M, tid * per);
-    const int e = min(M, b + per);
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int groups = M >> 2;
+    const int per = (groups + kScanThreads - 1) / kScanThreads;
+    const int b = min(groups, tid * per);
+    const int e = min(groups, b + per);
+    i4 *hv = reinterpret_cast<i4 *>(h);
+    i4 keep[kBatch];
     int sum = 0;
-    for (int j = b; j < e; ++j)
-        sum += h[j];
-    part[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        const int v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
+    for (int j0 = b; j0 < e; j0 += kBatch) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            keep[u] = j0 + u < e ? hv[j0 + u] : i4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            sum += keep[u][0] + keep[u][1] + keep[u][2] + keep[u][3];
     }
-    int run = part[tid] - sum;
-    for (int j = b; j < e; ++j) {
-        const int v = h[j];
-        h[j] = run;
-        run += v;
+    // Block-wide exclusive prefix of the per-thread sums: within each wave by
+    // shuffles, then across the 16 wave totals.
+    int x = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off)
+            x += y;
+    }
+    if (lane == 63)
+        wtot[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        int t = lane < kScanThreads / 64 ? wtot[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kScanThreads / 64; off <<= 1) {
+            const int y = __shfl_up(t, off);
+            if (lane >= off)
+                t += y;
+        }
+        if (lane < kScanThreads / 64)     // same wave: its reads came first
+            wtot[lane] = t;
+    }
+    __syncthreads();
+    int run = x - sum + (w > 0 ? wtot[w - 1] : 0);
+    auto put = [&](int j, const i4 &v) __attribute__((always_inline)) {
+        i4 o;
+        o[0] = run;
+        o[1] = run + v[0];
+        o[2] = o[1] + v[1];
+        o[3] = o[2] + v[2];
+        run = o[3] + v[3];
+        hv[j] = o;
+    };
+    if (per <= kBatch) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (b + u < e)
+                put(b + u, keep[u]);
+    } else {
+        for (int j0 = b; j0 < e; j0 += kBatch) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                keep[u] = j0 + u < e ? hv[j0 + u] : i4{0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (j0 + u < e)
+                    put(j0 + u, keep[u]);
+        }
     }
 }
 
-// One stable scatter pass on digit (key >> shift) & 255.  FIRST: keys come
-// from the labels and values are the point indices.  hist_next (null on the
-// last pass) collects the next digit per destination tile.
-template <bool FIRST>
-__global__ __launch_bounds__(kSortThreads)
+// One stable scatter pass on digit (key >> shift) & 255.  hist is this
+// pass's histogram ([digit][stride]); SCANNED: it holds exclusive offsets
+// already (the scan kernel ran), else each workgroup derives its own 256
+// offsets from the raw counts (four threads sum each digit's row, the
+// digits' totals are prefix-summed across the first four waves).  FIRST: keys come
+// from the labels and the values are the point indices.
+//
+// A round places 1024 keys (16 waves): each wave finds the lanes sharing
+// its digit with 8 ballots (rank = earlier such lanes) and the group's last
+// lane records the count, tagged with the round, in wcnt[wave][digit]; the
+// owner thread of each digit then turns the 16 counts into per-wave starts
+// (its running position plus the counts of earlier waves).
+template <bool FIRST, bool SCANNED>
+__global__ __launch_bounds__(kScatterThreads)
 void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__restrict__ vals_in,
-                        int N, int K, int shift, int tile_log2, int tiles,
-                        const int32_t *__restrict__ offs, int32_t *__restrict__ keys_out,
-                        int32_t *__restrict__ vals_out, int32_t *__restrict__ hist_next) {
-    __shared__ int running[kRadix];
-    __shared__ int wcnt[kSortThreads / 64][kRadix];   // (round tag << 8) | count
+                        int N, int K, int shift, int tile_log2, int tiles, int stride,
+                        const int32_t *__restrict__ hist, int32_t *__restrict__ keys_out,
+                        int32_t *__restrict__ vals_out) {
+    typedef int32_t i4 __attribute__((ext_vector_type(4)));
+    constexpr int kWaves = kScatterThreads / 64;
+    __shared__ int wcnt[kWaves][kRadix];   // (round tag << 8) | count
+    __shared__ int wpos[kWaves][kRadix];   // first position of (wave, digit) this round
+    __shared__ int wsum[4];
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int t = blockIdx.x;
-    running[tid] = offs[static_cast<size_t>(tid) * tiles + t];
+    const bool owner = tid < kRadix;       // thread d < 256 owns digit d
+    int run = 0;                           // owner: next position of its digit
+    if (SCANNED) {
+        if (owner)
+            run = hist[static_cast<size_t>(tid) * stride + t];
+    } else {
+        // Digit d's counts in earlier tiles and in all tiles (stride <= 128):
+        // four threads per digit each sum a quarter of its row.
+        const int d = tid & (kRadix - 1);
+        const int qq = tid >> 8;
+        constexpr int kG = kFusedScanTiles / 16;        // 16-byte groups per quarter
+        const i4 *rv = reinterpret_cast<const i4 *>(hist + static_cast<size_t>(d) * stride) +
+                       qq * kG;
+        i4 v[kG];
 #pragma unroll
-    for (int i = 0; i < kSortThreads / 64; ++i)
-        wcnt[i][tid] = 0;
+        for (int g = 0; g < kG; ++g)
+            v[g] = (qq * kG + g) * 4 < stride ? rv[g] : i4{0, 0, 0, 0};
+        int pre = 0, tot = 0;
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                tot += v[g][c];
+                pre += (qq * kG + g) * 4 + c < t ? v[g][c] : 0;
+            }
+        }
+        wpos[qq][d] = pre;
+        wcnt[qq][d] = tot;
+        __syncthreads();
+        int x = 0;
+        if (owner) {
+            pre = wpos[0][tid] + wpos[1][tid] + wpos[2][tid] + wpos[3][tid];
+            tot = wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+            x = tot;                       // inclusive prefix over digits
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(x, off);
+                if (lane >= off)
+                    x += y;
+            }
+            if (lane == 63)
+                wsum[w] = x;
+        }
+        __syncthreads();
+        if (owner) {
+            run = x - tot + pre;
+            for (int v2 = 0; v2 < w; ++v2)
+                run += wsum[v2];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kWaves * kRadix / kScatterThreads; ++i)
+        (&wcnt[0][0])[tid + i * kScatterThreads] = 0;
     __syncthreads();
     const int beg = t << tile_log2;
     const int fin = static_cast<int>(min(static_cast<int64_t>(N),
                                          static_cast<int64_t>(beg) + (int64_t(1) << tile_log2)));
     const uint64_t below = (uint64_t(1) << lane) - 1;
     int tag = 0;
-    for (int base = beg; base < fin; base += kSortThreads) {
-        ++tag;
-        const int i = base + tid;
-        const bool valid = i < fin;
-        int key = 0, val = 0;
-        if (valid) {
-            key = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
-            val = FIRST ? i : vals_in[i];
-        }
-        const int d = (key >> shift) & (kRadix - 1);
-        // Lanes of this wave holding the same digit.
-        uint64_t same = __ballot(valid);
+    // Keys and values are loaded kBatchRounds rounds at a time, all loads of
+    // a batch in flight together; the rounds then touch only LDS.
+    for (int base0 = beg; base0 < fin; base0 += kBatchRounds * kScatterThreads) {
+        int bkey[kBatchRounds], bval[kBatchRounds];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const bool bit = (d >> b) & 1;
-            const uint64_t m = __ballot(valid && bit);
-            same &= bit ? m : ~m;
-        }
-        if (valid && (same >> lane) == 1)              // last lane of its group
-            wcnt[w][d] = (tag << 8) | __popcll(same);
-        __syncthreads();
-        if (valid) {
-            int pos = running[d] + __popcll(same & below);
-            for (int v = 0; v < w; ++v) {
-                const int e = wcnt[v][d];
-                pos += (e >> 8) == tag ? (e & 255) : 0;
+        for (int r = 0; r < kBatchRounds; ++r) {
+            const int i = base0 + r * kScatterThreads + tid;
+            bkey[r] = 0;
+            bval[r] = 0;
+            if (i < fin) {
+                bkey[r] = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
+                bval[r] = FIRST ? i : vals_in[i];
             }
-            keys_out[pos] = key;
-            vals_out[pos] = val;
-            if (hist_next)
-                atomicAdd(&hist_next[static_cast<size_t>((key >> (shift + 8)) & (kRadix - 1)) *
-                                         tiles + (pos >> tile_log2)], 1);
         }
-        int tot = 0;
 #pragma unroll
-        for (int v = 0; v < kSortThreads / 64; ++v) {
-            const int e = wcnt[v][tid];
-            tot += (e >> 8) == tag ? (e & 255) : 0;
+        for (int r = 0; r < kBatchRounds; ++r) {
+            const int base = base0 + r * kScatterThreads;
+            if (base >= fin)
+                break;                         // uniform: the tile ends here
+            ++tag;
+            const bool valid = base + tid < fin;
+            const int key = bkey[r];
+            const int d = (key >> shift) & (kRadix - 1);
+            uint64_t same = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const bool bit = (d >> b) & 1;
+                const uint64_t m = __ballot(valid && bit);
+                same &= bit ? m : ~m;
+            }
+            if (valid && (same >> lane) == 1)          // last lane of its group
+                wcnt[w][d] = (tag << 8) | __popcll(same);
+            __syncthreads();
+            if (owner) {
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) {
+                    const int e = wcnt[v][tid];
+                    wpos[v][tid] = run;
+                    run += (e >> 8) == tag ? (e & 255) : 0;
+                }
+            }
+            __syncthreads();
+            if (valid) {
+                const int pos = wpos[w][d] + __popcll(same & below);
+                keys_out[pos] = key;
+                vals_out[pos] = bval[r];
+            }
         }
-        __syncthreads();
-        running[tid] += tot;
     }
 }
 
@@ -268,13 +403,16 @@ __device__ __forceinline__ void emit_cluster(int k, const uint32_t (&bits)[V], c
         for (int v = 0; v < V; ++v)
             lds_row[lane * V + v] = static_cast<uint16_t>(bits[v]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");   // row copy visible to the wave
+    // The wave's own LDS writes are seen by its later LDS reads (LDS runs a
+    // wave's operations in order); the barrier keeps the compiler from
+    // moving the reads above the writes.
+    __builtin_amdgcn_wave_barrier();
     const float n = row_sq_norm16(lds_row, D, lane & 15);
     if (lane == 0) {
         norms[k] = n;
         counts[k] = count;
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");   // reads done before the next copy
+    __builtin_amdgcn_wave_barrier();
 }
 
 template <int V>
@@ -293,113 +431,162 @@ __device__ __forceinline__ void emit_mean(int k, const float (&sum)[V], int coun
     emit_cluster<V>(k, bits, mean, count, D, lane, lds_row, C_new, means, norms, counts);
 }
 
-// Runs of equal keys over one chunk of sorted positions per wave.  For a run
-// [a, b) of cluster k: a is k's first position unless the run starts the
-// chunk and the previous position holds k too; b is its end unless the run
-// ends the chunk and the next position holds k too.  A run that is the whole
-// cluster is finished here; otherwise its sum goes to partial slot 0 (the run
-// began before this chunk) or 1 (it began here and continues past it).
 template <int V>
-__global__ __launch_bounds__(64 * kReduceWaves)
+__device__ __forceinline__ RowBits<V> lds_row_bits(const uint16_t *p) {
+    RowBits<V> r;
+    if constexpr (V == 1) {
+        r.w[0] = *p;
+    } else if constexpr (V == 2) {
+        r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+    } else if constexpr (V == 4) {
+        typedef uint32_t w2 __attribute__((ext_vector_type(2)));
+        const w2 v = *reinterpret_cast<const w2 *>(p);
+        r.w[0] = v[0];
+        r.w[1] = v[1];
+    } else {
+        typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+        const w4 v = *reinterpret_cast<const w4 *>(p);
+        r.w[0] = v[0];
+        r.w[1] = v[1];
+        r.w[2] = v[2];
+        r.w[3] = v[3];
+    }
+    return r;
+}
+
+// One chunk of P sorted positions per workgroup.  The chunk's keys, point
+// indices and rows are staged in LDS first (the row loads of the whole
+// chunk are in flight together); then each wave takes the runs of equal
+// keys that start in its 64-position stripes (stripe s -> wave s % 4) and
+// sums each run's rows from LDS in position order.  For a run [a, b) of
+// cluster k: a is k's first position unless the run starts the chunk and
+// the position before holds k too; b is its end unless the run ends the
+// chunk and the position after holds k too.  A run that is the whole
+// cluster is finished here; otherwise its sum goes to partial slot 0 (the
+// run began before this chunk) or 1 (it began here and continues past it).
+template <int V>
+__global__ __launch_bounds__(kReduceThreads, 4)
 void upd_reduce_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ keys,
-                       const int32_t *__restrict__ vals, int N, int D, int K,
-                       int32_t *__restrict__ start, int32_t *__restrict__ end,
+                       const int32_t *__restrict__ vals, int N, int D, int K, int P,
+                       int cpr_inv, int32_t *__restrict__ start, int32_t *__restrict__ end,
                        float *__restrict__ partial, uint16_t *__restrict__ C_new,
                        float *__restrict__ means, float *__restrict__ norms,
                        int32_t *__restrict__ counts) {
-    __shared__ uint16_t lds[kReduceWaves][kMaxRow];
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int chunk = blockIdx.x * kReduceWaves + wave;
-    const int c0 = chunk * kUpdateChunk;
-    if (c0 >= N)
-        return;
-    const int c1 = min(N, c0 + kUpdateChunk);
+    typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint16_t rows[kStageBytes / 2];
+    __shared__ int skey[kMaxChunk];
+    __shared__ int sval[kMaxChunk];
+    __shared__ __attribute__((aligned(16))) uint16_t nrow[kReduceThreads / 64][kMaxRow];
+    __shared__ int edge[2];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int chunk = blockIdx.x;
+    const int c0 = chunk * P;
+    const int n = min(N - c0, P);
+    for (int j = tid; j < n; j += kReduceThreads) {
+        skey[j] = keys[c0 + j];
+        sval[j] = vals[c0 + j];
+    }
+    if (tid == 0) {
+        edge[0] = c0 > 0 ? keys[c0 - 1] : -1;
+        edge[1] = c0 + n < N ? keys[c0 + n] : -1;
+    }
+    __syncthreads();
+
+    // Stage the rows: 16-byte piece q is column (q % cpr) * 8 of row q / cpr
+    // (q / cpr as (q * cpr_inv) >> 20, exact for q < 4096 and cpr <= 64).
+    // Rows of stray labels are staged too (they are point rows all the same)
+    // and never read.
+    const int cpr = D >> 3;
+    const int pieces = n * cpr;
+    w4 buf[kStagePieces];
+#pragma unroll
+    for (int i = 0; i < kStagePieces; ++i) {
+        const int q = tid + i * kReduceThreads;
+        buf[i] = w4{0u, 0u, 0u, 0u};
+        if (q < pieces) {
+            const int r = (q * cpr_inv) >> 20;
+            buf[i] = *reinterpret_cast<const w4 *>(X + static_cast<size_t>(sval[r]) * D +
+                                                   (q - r * cpr) * 8);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kStagePieces; ++i) {
+        const int q = tid + i * kReduceThreads;
+        if (q < pieces)
+            *reinterpret_cast<w4 *>(rows + q * 8) = buf[i];
+    }
+    __syncthreads();
+
     const bool on = lane * V < D;
-    const uint16_t *xl = X + lane * V;
-    uint16_t *lds_row = lds[wave];
-
-    int cur = keys[c0];
-    if (cur >= K)
-        return;                         // only stray labels from here on
-    int run_start = c0;
-    float acc[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-        acc[v] = 0.0f;
-
-    auto flush = [&](int b) __attribute__((always_inline)) {
-        const bool before = run_start == c0 && c0 > 0 && keys[c0 - 1] == cur;
-        const bool after = b == c1 && c1 < N && keys[c1] == cur;
-        if (lane == 0) {
-            if (!before)
-                start[cur] = run_start;
-            if (!after)
-                end[cur] = b;
-        }
-        if (!before && !after) {
-            emit_mean<V>(cur, acc, b - run_start, D, lane, lds_row, C_new, means, norms, counts);
-        } else if (on) {
-            float *dst = partial + (static_cast<size_t>(chunk) * 2 + (before ? 0 : 1)) * D + lane * V;
-            store_f32<V>(dst, acc);
-        }
-    };
-
-    // Positions past the chunk read as key K, like stray labels: either ends
-    // the walk.  Keys and indices are wave-uniform (scalar registers).
-    bool done = false;
-    for (int p = c0; p < c1 && !done; p += kPrefetch) {
-        int kk[kPrefetch];
-        RowBits<V> rb[kPrefetch];
-#pragma unroll
-        for (int u = 0; u < kPrefetch; ++u) {
-            const int q = p + u;
-            kk[u] = q < c1 ? __builtin_amdgcn_readfirstlane(keys[q]) : K;
-            const int idx = kk[u] < K ? __builtin_amdgcn_readfirstlane(vals[q]) : -1;
-            rb[u] = (on && idx >= 0) ? load_row<V>(xl + static_cast<size_t>(idx) * D)
-                                     : RowBits<V>{};
-        }
-#pragma unroll
-        for (int u = 0; u < kPrefetch; ++u) {
-            if (!done && kk[u] != cur) {
-                flush(p + u);
-                if (kk[u] >= K) {
-                    done = true;
-                } else {
-                    cur = kk[u];
-                    run_start = p + u;
-#pragma unroll
-                    for (int v = 0; v < V; ++v)
-                        acc[v] = 0.0f;
+    uint16_t *lds_row = nrow[wave];
+    for (int st = wave; st * 64 < n; st += kReduceThreads / 64) {
+        const int j = st * 64 + lane;
+        const int kj = j < n ? skey[j] : K;
+        uint64_t starts = __ballot(j < n && kj < K && (j == 0 || skey[j - 1] != kj));
+        while (starts) {
+            const int a = st * 64 + __builtin_ctzll(starts);
+            starts &= starts - 1;
+            const int k = __builtin_amdgcn_readfirstlane(skey[a]);
+            int b = n;
+            for (int base = a + 1; base < n; base += 64) {
+                const int q = base + lane;
+                const uint64_t diff = __ballot(q < n && skey[q] != k);
+                if (diff) {
+                    b = base + __builtin_ctzll(diff);
+                    break;
                 }
             }
-            if (!done) {
+            float acc[V];
 #pragma unroll
-                for (int v = 0; v < V; ++v)
-                    acc[v] += row_value<V>(rb[u], v);
+            for (int v = 0; v < V; ++v)
+                acc[v] = 0.0f;
+            if (on) {
+                const uint16_t *src = rows + lane * V;
+#pragma unroll 8
+                for (int p = a; p < b; ++p) {
+                    const RowBits<V> r = lds_row_bits<V>(src + p * D);
+#pragma unroll
+                    for (int v = 0; v < V; ++v)
+                        acc[v] += row_value<V>(r, v);
+                }
+            }
+            const bool before = a == 0 && edge[0] == k;
+            const bool after = b == n && edge[1] == k;
+            if (lane == 0) {
+                if (!before)
+                    start[k] = c0 + a;
+                if (!after)
+                    end[k] = c0 + b;
+            }
+            if (!before && !after) {
+                emit_mean<V>(k, acc, b - a, D, lane, lds_row, C_new, means, norms, counts);
+            } else if (on) {
+                float *dst = partial + (static_cast<size_t>(chunk) * 2 + (before ? 0 : 1)) * D +
+                             lane * V;
+                store_f32<V>(dst, acc);
             }
         }
     }
-    if (!done)
-        flush(c1);
 }
 
 // Clusters the reduce kernel did not finish: empty ones (old row kept) and
 // those spanning several chunks (partials added in chunk order).
 template <int V>
-__global__ __launch_bounds__(64 * kReduceWaves)
+__global__ __launch_bounds__(kReduceThreads)
 void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__restrict__ start,
                        const int32_t *__restrict__ end, const float *__restrict__ partial,
-                       int N, int D, int K, uint16_t *__restrict__ C_new,
+                       int N, int D, int K, int P, uint16_t *__restrict__ C_new,
                        float *__restrict__ means, float *__restrict__ norms,
                        int32_t *__restrict__ counts) {
-    __shared__ uint16_t lds[kReduceWaves][kMaxRow];
+    __shared__ __attribute__((aligned(16))) uint16_t nrow[kReduceThreads / 64][kMaxRow];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const bool on = lane * V < D;
-    uint16_t *lds_row = lds[wave];
-    const int nwaves = gridDim.x * kReduceWaves;
-    for (int k = blockIdx.x * kReduceWaves + wave; k < K; k += nwaves) {
+    uint16_t *lds_row = nrow[wave];
+    const int nwaves = gridDim.x * (kReduceThreads / 64);
+    for (int k = blockIdx.x * (kReduceThreads / 64) + wave; k < K; k += nwaves) {
         const int s = N > 0 ? start[k] : 0;
         const int e = N > 0 ? end[k] : 0;
         const int count = e - s;
@@ -416,8 +603,8 @@ void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__rest
             emit_cluster<V>(k, bits, mean, 0, D, lane, lds_row, C_new, means, norms, counts);
             continue;
         }
-        const int cf = s / kUpdateChunk;
-        const int cl = (e - 1) / kUpdateChunk;
+        const int cf = s / P;
+        const int cl = (e - 1) / P;
         if (cf == cl)
             continue;                   // finished by the reduce kernel
         float sum[V];
@@ -442,18 +629,19 @@ hipError_t launch_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *k
                        const int32_t *vals, const uint16_t *C_old, int N, int D, int K,
                        int32_t *start, int32_t *end, float *partial, uint16_t *C_new,
                        float *norms, int32_t *counts, float *means, hipStream_t stream) {
-    const dim3 block(64 * kReduceWaves);
+    const dim3 block(kReduceThreads);
     if (N > 0) {
-        const int wgs = (pl.chunks + kReduceWaves - 1) / kReduceWaves;
-        hipLaunchKernelGGL(upd_reduce_kernel<V>, dim3(wgs), block, 0, stream, X, keys, vals, N, D,
-                           K, start, end, partial, C_new, means, norms, counts);
+        const int cpr_inv = ((1 << 20) + D / 8 - 1) / (D / 8);
+        hipLaunchKernelGGL(upd_reduce_kernel<V>, dim3(pl.chunks), block, 0, stream, X, keys, vals,
+                           N, D, K, pl.chunk, cpr_inv, start, end, partial, C_new, means, norms,
+                           counts);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    const int fin_wgs = min((K + kReduceWaves - 1) / kReduceWaves, 8192);
+    const int fin_wgs = min((K + 3) / 4, 8192);
     hipLaunchKernelGGL(upd_finish_kernel<V>, dim3(fin_wgs), block, 0, stream, C_old, start, end,
-                       partial, N, D, K, C_new, means, norms, counts);
+                       partial, N, D, K, pl.chunk, C_new, means, norms, counts);
     return hipGetLastError();
 }
 
@@ -465,12 +653,19 @@ UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K) {
     while ((int64_t(1) << bits) <= K)
         ++bits;                                   // keys run 0..K
     p.passes = (bits + 7) / 8;
-    int tl = 10;                                  // tiles of >= 1024 points,
-    while ((int64_t(1) << tl) * 4096 < N)         // at most 4096 tiles
+    // Sort tiles of 2^tl >= 1024 points: at most 128 tiles while tiles stay
+    // <= 16384 points (the scan then holds its histogram in registers), at
+    // most 4096 beyond.
+    int tl = 10;
+    while (tl < 14 && (int64_t(1) << tl) * 128 < N)
+        ++tl;
+    while ((int64_t(1) << tl) * 4096 < N)
         ++tl;
     p.tile_log2 = tl;
     p.tiles = static_cast<int>((N + (int64_t(1) << tl) - 1) >> tl);
-    p.chunks = static_cast<int>((N + kUpdateChunk - 1) / kUpdateChunk);
+    p.stride = (p.tiles + 3) & ~3;
+    p.chunk = static_cast<int>(min(static_cast<int64_t>(kMaxChunk), kStageBytes / (2 * D)));
+    p.chunks = static_cast<int>((N + p.chunk - 1) / p.chunk);
     if (N == 0)
         return p;
     size_t off = 0;
@@ -482,7 +677,7 @@ UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K) {
         off += n4;
     }
     p.hist = off;
-    off += align_up(static_cast<size_t>(p.passes) * kRadix * p.tiles * 4);
+    off += align_up(static_cast<size_t>(p.passes) * kRadix * p.stride * 4);
     p.start = off;
     off += align_up(static_cast<size_t>(K) * 4);
     p.end = off;
@@ -505,41 +700,47 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
         end = reinterpret_cast<int32_t *>(base + pl.end);
         partial = reinterpret_cast<float *>(base + pl.partial);
         auto *hist = reinterpret_cast<int32_t *>(base + pl.hist);
-        const size_t hsz = static_cast<size_t>(kRadix) * pl.tiles;
-        // start and end are adjacent in the workspace; clear both at once.
-        hipLaunchKernelGGL(upd_hist_kernel, dim3(pl.tiles), dim3(kSortThreads), 0, stream, labels,
-                           N, K, pl.tile_log2, pl.tiles, hist, start,
-                           static_cast<int64_t>((pl.partial - pl.start) / 4), hist + hsz,
-                           static_cast<int64_t>(hsz * (pl.passes - 1)));
-        hipError_t e = hipGetLastError();
+        const size_t hsz = static_cast<size_t>(kRadix) * pl.stride;
+        const bool scan = pl.tiles > kFusedScanTiles;
+        const dim3 grid(pl.tiles), block(kSortThreads);
+        hipError_t e = hipSuccess;
         for (int q = 0; q < pl.passes && e == hipSuccess; ++q) {
             int32_t *h = hist + hsz * q;
-            hipLaunchKernelGGL(upd_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, h,
-                               static_cast<int>(hsz));
-            e = hipGetLastError();
-            if (e != hipSuccess)
-                break;
             const int32_t *kin = q == 0 ? labels : reinterpret_cast<int32_t *>(base + pl.keys[(q - 1) & 1]);
             const int32_t *vin = q == 0 ? nullptr : reinterpret_cast<int32_t *>(base + pl.vals[(q - 1) & 1]);
             keys = reinterpret_cast<int32_t *>(base + pl.keys[q & 1]);
             vals = reinterpret_cast<int32_t *>(base + pl.vals[q & 1]);
-            int32_t *hn = q + 1 < pl.passes ? h + hsz : nullptr;
-            if (q == 0)
-                hipLaunchKernelGGL(upd_scatter_kernel<true>, dim3(pl.tiles), dim3(kSortThreads), 0,
-                                   stream, kin, vin, N, K, 8 * q, pl.tile_log2, pl.tiles, h, keys,
-                                   vals, hn);
+            if (q == 0)   // also clears start and end (adjacent in the workspace)
+                hipLaunchKernelGGL(upd_hist_kernel<true>, grid, block, 0, stream, kin, N, K, 0,
+                                   pl.tile_log2, pl.tiles, pl.stride, h, start,
+                                   static_cast<int64_t>((pl.partial - pl.start) / 4));
             else
-                hipLaunchKernelGGL(upd_scatter_kernel<false>, dim3(pl.tiles), dim3(kSortThreads), 0,
-                                   stream, kin, vin, N, K, 8 * q, pl.tile_log2, pl.tiles, h, keys,
-                                   vals, hn);
+                hipLaunchKernelGGL(upd_hist_kernel<false>, grid, block, 0, stream, kin, N, K, 8 * q,
+                                   pl.tile_log2, pl.tiles, pl.stride, h, nullptr, int64_t(0));
+            if (scan)
+                hipLaunchKernelGGL(upd_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, h,
+                                   static_cast<int>(hsz));
+            const int sh = 8 * q;
+            const dim3 sblock(kScatterThreads);
+            if (q == 0 && scan)
+                hipLaunchKernelGGL((upd_scatter_kernel<true, true>), grid, sblock, 0, stream, kin,
+                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
+            else if (q == 0)
+                hipLaunchKernelGGL((upd_scatter_kernel<true, false>), grid, sblock, 0, stream, kin,
+                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
+            else if (scan)
+                hipLaunchKernelGGL((upd_scatter_kernel<false, true>), grid, sblock, 0, stream, kin,
+                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
+            else
+                hipLaunchKernelGGL((upd_scatter_kernel<false, false>), grid, sblock, 0, stream, kin,
+                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
             e = hipGetLastError();
         }
         if (e != hipSuccess)
             return e;
     }
-    if (D <= 64)
-        return launch_sums<1>(pl, X, keys, vals, C_old, N, D, K, start, end, partial, C_new, norms,
-                              counts, means, stream);
+    // Two columns per lane up to D = 128 (D / 2 lanes active below 128): a
+    // one-column variant needs several times the registers for no gain.
     if (D <= 128)
         return launch_sums<2>(pl, X, keys, vals, C_old, N, D, K, start, end, partial, C_new, norms,
                               counts, means, stream);

@@ -40,7 +40,8 @@ BF16_DENSE_PEAK_TFLOPS = 2516.6     # MI355X: 256 CU x 4096 flop/clk x 2.4 GHz
 KERNEL_SOURCES = ("means_nearest_centroid_amd/csrc/kmeans_kernels.hip",
                   "means_nearest_centroid_amd/csrc/kmeans_internal.h",
                   "means_nearest_centroid_amd/csrc/kmeans_api.hip")
-UPDATE_SOURCES = KERNEL_SOURCES + ("means_nearest_centroid_amd/csrc/kmeans_update.hip",)
+UPDATE_SOURCES = KERNEL_SOURCES + ("means_nearest_centroid_amd/csrc/kmeans_update.hip",
+                                   "means_nearest_centroid_amd/csrc/kmeans_update_internal.h")
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 
 

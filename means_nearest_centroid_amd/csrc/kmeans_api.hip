@@ -10,8 +10,10 @@
 #include "kmeans_mi355x.h"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+namespace kmeans {
 
 kmeans_status_t fail(kmeans_status_t st, const char *fmt, ...) {
     char buf[512];
@@ -30,21 +32,17 @@ kmeans_status_t ok() {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-constexpr int64_t kMaxRows = 0x7fffffffLL - 1024;   // int32 indexing headroom
-
-// Compute units of the current device (cached per device), or the MI355X
-// count when it cannot be queried.
 int device_compute_units() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return kmeans::kDefaultComputeUnits;
+        return kDefaultComputeUnits;
     int cus = cache[dev].load(std::memory_order_relaxed);
     if (cus <= 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
-            cus = kmeans::kDefaultComputeUnits;
+            cus = kDefaultComputeUnits;
         cache[dev].store(cus, std::memory_order_relaxed);
     }
     return cus;
@@ -57,6 +55,17 @@ kmeans_status_t check_d(int64_t D) {
                     static_cast<long long>(D), KMEANS_MIN_D, KMEANS_MAX_D);
     return KMEANS_OK;
 }
+
+}  // namespace kmeans
+
+namespace {
+
+using kmeans::aligned;
+using kmeans::check_d;
+using kmeans::device_compute_units;
+using kmeans::fail;
+using kmeans::kMaxRows;
+using kmeans::ok;
 
 kmeans_status_t check_shape(int64_t N, int64_t D, int64_t K) {
     if (N < 0)
@@ -211,51 +220,6 @@ kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_uni
         *k_block = pl.bk;
     if (padded_d)
         *padded_d = pl.ks * 16;
-    return ok();
-}
-
-kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
-                              int64_t N, int64_t D, int64_t K, void *C_new, float *norms,
-                              int32_t *counts, float *means, hipStream_t stream) {
-    if (N < 0)
-        return fail(KMEANS_ERR_INVALID_ARG, "N=%lld must be >= 0", static_cast<long long>(N));
-    if (K < 1)
-        return fail(KMEANS_ERR_INVALID_ARG, "K=%lld must be >= 1", static_cast<long long>(K));
-    kmeans_status_t st = check_d(D);
-    if (st != KMEANS_OK)
-        return st;
-    if (N > kMaxRows || K > kMaxRows)
-        return fail(KMEANS_ERR_UNSUPPORTED, "N=%lld or K=%lld too large (max %lld)",
-                    static_cast<long long>(N), static_cast<long long>(K),
-                    static_cast<long long>(kMaxRows));
-    if (!C_old || !C_new || !norms || !counts || (N > 0 && (!X || !labels)))
-        return fail(KMEANS_ERR_INVALID_ARG, "null pointer argument (X=%p labels=%p C_old=%p "
-                    "C_new=%p norms=%p counts=%p)", X, static_cast<const void *>(labels), C_old,
-                    C_new, static_cast<void *>(norms), static_cast<void *>(counts));
-    if ((N > 0 && !aligned(X, 16)) || !aligned(C_old, 16) || !aligned(C_new, 16))
-        return fail(KMEANS_ERR_ALIGNMENT, "X, C_old and C_new must be 16-byte aligned");
-    if ((N > 0 && !aligned(labels, 4)) || !aligned(norms, 4) || !aligned(counts, 4) ||
-        !aligned(means, 4))
-        return fail(KMEANS_ERR_ALIGNMENT, "labels, norms, counts and means must be 4-byte aligned");
-
-    const kmeans::UpdatePlan pl = kmeans::make_update_plan(N, D, K);
-    void *ws = nullptr;
-    if (pl.bytes > 0) {
-        hipError_t e = hipMallocAsync(&ws, pl.bytes, stream);
-        if (e != hipSuccess || ws == nullptr)
-            return fail(KMEANS_ERR_NO_MEMORY, "hipMallocAsync(%zu) failed: %s", pl.bytes,
-                        hipGetErrorString(e));
-    }
-    hipError_t e = kmeans::launch_update(pl, static_cast<const uint16_t *>(X), labels,
-                                         static_cast<const uint16_t *>(C_old),
-                                         static_cast<int>(N), static_cast<int>(D),
-                                         static_cast<int>(K), static_cast<uint16_t *>(C_new),
-                                         norms, counts, means, ws, stream);
-    hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
-    if (e != hipSuccess)
-        return fail(KMEANS_ERR_HIP, "update launch failed: %s", hipGetErrorString(e));
-    if (ef != hipSuccess)
-        return fail(KMEANS_ERR_HIP, "hipFreeAsync failed: %s", hipGetErrorString(ef));
     return ok();
 }
 

@@ -1,9 +1,11 @@
 // kmeans_internal.h -- launch plan and launchers shared by the C ABI layer
-// and the kernel translation unit.  Not part of the public interface.
+// and the kernel translation units.  Not part of the public interface.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "kmeans_mi355x.h"
 
 namespace kmeans {
 
@@ -102,33 +104,6 @@ __device__ __forceinline__ float row_sq_norm16(const uint16_t *row, int D, int l
     return acc;
 }
 
-// ---- centroid update (the step after assignment in a Lloyd iteration) ----
-
-// Workspace layout and launch shape of one kmeans_update call.
-struct UpdatePlan {
-    int passes;        // 8-bit radix passes over the keys 0..K (K = stray label)
-    int tile_log2;     // sort tile of 2^tile_log2 points (>= 1024)
-    int tiles;         // sort tiles
-    int stride;        // histogram row length: tiles rounded up to 4
-    int chunk;         // sorted positions per reduce chunk (64 KiB of rows, <= 1024)
-    int chunks;        // reduce chunks
-    size_t keys[2], vals[2];   // byte offsets of the ping-pong sort buffers
-    size_t hist;       // [passes][256][stride] int32
-    size_t start, end; // [K] int32 each
-    size_t partial;    // [chunks][2][D] fp32
-    size_t bytes;      // total workspace (0 when N == 0)
-};
-
-// Requires 0 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller).
-UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K);
-
-// All launches of one update on `stream`; ws holds plan.bytes bytes (may be
-// null when N == 0).  means may be null.
-hipError_t launch_update(const UpdatePlan &plan, const uint16_t *X, const int32_t *labels,
-                         const uint16_t *C_old, int N, int D, int K, uint16_t *C_new,
-                         float *norms, int32_t *counts, float *means, void *ws,
-                         hipStream_t stream);
-
 // Direct path when ws_score == nullptr, otherwise writes per-split partial
 // winners to the workspace and the merge kernel finishes.
 hipError_t launch_assign(const Plan &plan, const uint16_t *X, const uint16_t *C,
@@ -140,5 +115,19 @@ hipError_t launch_merge(const Plan &plan, const uint16_t *X, const uint16_t *C,
                         const float *norms, int N, int D, int K, int32_t *labels,
                         float *min_dist, const float *ws_score, const int32_t *ws_label,
                         const float *ws_xx, hipStream_t stream);
+
+// ---- C ABI helpers shared by the entry points (kmeans_api.hip) ----
+
+constexpr int64_t kMaxRows = 0x7fffffffLL - 1024;   // int32 indexing headroom
+
+// Record a thread-local message for kmeans_last_error and return st.
+kmeans_status_t fail(kmeans_status_t st, const char *fmt, ...);
+// Clear the message and return KMEANS_OK.
+kmeans_status_t ok();
+bool aligned(const void *p, uintptr_t a);
+// KMEANS_ERR_UNSUPPORTED unless 16 <= D <= 512 and D % 16 == 0.
+kmeans_status_t check_d(int64_t D);
+// Compute units of the current device (cached per device), or 256.
+int device_compute_units();
 
 }  // namespace kmeans

@@ -37,7 +37,7 @@
 //     pre-pass computes it (row_sq_norm16 over a copy of the row in LDS).
 #include <stdint.h>
 
-#include "kmeans_internal.h"
+#include "kmeans_update_internal.h"
 
 namespace kmeans {
 namespace {
@@ -54,7 +54,7 @@ constexpr int kMaxRow = 512;         // bf16 values of the widest supported row
 // a CU (1024 at once on 256 CUs); 8 loads of 16 bytes per thread fill it.
 constexpr int kStageBytes = 32768;
 constexpr int kStagePieces = kStageBytes / 16 / kReduceThreads;
-constexpr int kMaxChunk = 480;        // keeps a reduce workgroup within 40 KiB of LDS
+constexpr int kMaxChunk = 240;        // keeps a reduce workgroup within 40 KiB of LDS
 
 __device__ __forceinline__ int sort_key(int32_t label, int K) {
     return (label < 0 || label >= K) ? K : label;
@@ -213,6 +213,26 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int t = blockIdx.x;
+    const int beg = t << tile_log2;
+    const int fin = static_cast<int>(min(static_cast<int64_t>(N),
+                                         static_cast<int64_t>(beg) + (int64_t(1) << tile_log2)));
+    // Keys and values are loaded kBatchRounds rounds at a time, all loads of
+    // a batch in flight together; the first batch is issued before the
+    // offsets are worked out, so the two sets of loads overlap.
+    int bkey[kBatchRounds], bval[kBatchRounds];
+    auto load_batch = [&](int base0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < kBatchRounds; ++r) {
+            const int i = base0 + r * kScatterThreads + tid;
+            bkey[r] = 0;
+            bval[r] = 0;
+            if (i < fin) {
+                bkey[r] = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
+                bval[r] = FIRST ? i : vals_in[i];
+            }
+        }
+    };
+    load_batch(beg);
     const bool owner = tid < kRadix;       // thread d < 256 owns digit d
     int run = 0;                           // owner: next position of its digit
     if (SCANNED) {
@@ -267,25 +287,11 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
     for (int i = 0; i < kWaves * kRadix / kScatterThreads; ++i)
         (&wcnt[0][0])[tid + i * kScatterThreads] = 0;
     __syncthreads();
-    const int beg = t << tile_log2;
-    const int fin = static_cast<int>(min(static_cast<int64_t>(N),
-                                         static_cast<int64_t>(beg) + (int64_t(1) << tile_log2)));
     const uint64_t below = (uint64_t(1) << lane) - 1;
     int tag = 0;
-    // Keys and values are loaded kBatchRounds rounds at a time, all loads of
-    // a batch in flight together; the rounds then touch only LDS.
     for (int base0 = beg; base0 < fin; base0 += kBatchRounds * kScatterThreads) {
-        int bkey[kBatchRounds], bval[kBatchRounds];
-#pragma unroll
-        for (int r = 0; r < kBatchRounds; ++r) {
-            const int i = base0 + r * kScatterThreads + tid;
-            bkey[r] = 0;
-            bval[r] = 0;
-            if (i < fin) {
-                bkey[r] = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
-                bval[r] = FIRST ? i : vals_in[i];
-            }
-        }
+        if (base0 != beg)
+            load_batch(base0);
 #pragma unroll
         for (int r = 0; r < kBatchRounds; ++r) {
             const int base = base0 + r * kScatterThreads;
@@ -454,120 +460,173 @@ __device__ __forceinline__ RowBits<V> lds_row_bits(const uint16_t *p) {
     return r;
 }
 
-// One chunk of P sorted positions per workgroup.  The chunk's keys, point
-// indices and rows are staged in LDS first (the row loads of the whole
-// chunk are in flight together); then each wave takes the runs of equal
-// keys that start in its 64-position stripes (stripe s -> wave s % 4) and
-// sums each run's rows from LDS in position order.  For a run [a, b) of
-// cluster k: a is k's first position unless the run starts the chunk and
-// the position before holds k too; b is its end unless the run ends the
-// chunk and the position after holds k too.  A run that is the whole
-// cluster is finished here; otherwise its sum goes to partial slot 0 (the
-// run began before this chunk) or 1 (it began here and continues past it).
+// Chunks of P sorted positions; workgroup b takes chunks b, b + G, ... (G
+// workgroups, four per CU).  A chunk's keys, point indices and rows are
+// staged in LDS (all row loads of a chunk in flight at once), then each
+// wave takes the runs of equal keys that start in its 64-position stripes
+// (stripe s -> wave s % 4) and sums each run's rows from LDS in position
+// order.  Loads run ahead of the sums: while chunk c is summed, the rows of
+// the next chunk are on their way into registers and the keys of the one
+// after into registers too.
+//
+// For a run [a, b) of cluster k: a is k's first position unless the run
+// starts the chunk and the position before holds k too; b is its end unless
+// the run ends the chunk and the position after holds k too.  A run that is
+// the whole cluster is finished here; otherwise its sum goes to partial slot
+// 0 (the run began before this chunk) or 1 (it began here and continues).
 template <int V>
 __global__ __launch_bounds__(kReduceThreads, 4)
 void upd_reduce_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ keys,
-                       const int32_t *__restrict__ vals, int N, int D, int K, int P,
+                       const int32_t *__restrict__ vals, int N, int D, int K, int P, int chunks,
                        int cpr_inv, int32_t *__restrict__ start, int32_t *__restrict__ end,
                        float *__restrict__ partial, uint16_t *__restrict__ C_new,
                        float *__restrict__ means, float *__restrict__ norms,
                        int32_t *__restrict__ counts) {
     typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+    constexpr int kKeysPerThread = (kMaxChunk + kReduceThreads - 1) / kReduceThreads;
     __shared__ __attribute__((aligned(16))) uint16_t rows[kStageBytes / 2];
-    __shared__ int skey[kMaxChunk];
-    __shared__ int sval[kMaxChunk];
+    __shared__ int skey[2][kMaxChunk];
+    __shared__ int sval[2][kMaxChunk];
+    __shared__ int edge[2][2];
     __shared__ __attribute__((aligned(16))) uint16_t nrow[kReduceThreads / 64][kMaxRow];
-    __shared__ int edge[2];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int chunk = blockIdx.x;
-    const int c0 = chunk * P;
-    const int n = min(N - c0, P);
-    for (int j = tid; j < n; j += kReduceThreads) {
-        skey[j] = keys[c0 + j];
-        sval[j] = vals[c0 + j];
-    }
-    if (tid == 0) {
-        edge[0] = c0 > 0 ? keys[c0 - 1] : -1;
-        edge[1] = c0 + n < N ? keys[c0 + n] : -1;
-    }
-    __syncthreads();
-
-    // Stage the rows: 16-byte piece q is column (q % cpr) * 8 of row q / cpr
-    // (q / cpr as (q * cpr_inv) >> 20, exact for q < 4096 and cpr <= 64).
-    // Rows of stray labels are staged too (they are point rows all the same)
-    // and never read.
+    const int G = gridDim.x;
     const int cpr = D >> 3;
-    const int pieces = n * cpr;
-    w4 buf[kStagePieces];
-#pragma unroll
-    for (int i = 0; i < kStagePieces; ++i) {
-        const int q = tid + i * kReduceThreads;
-        buf[i] = w4{0u, 0u, 0u, 0u};
-        if (q < pieces) {
-            const int r = (q * cpr_inv) >> 20;
-            buf[i] = *reinterpret_cast<const w4 *>(X + static_cast<size_t>(sval[r]) * D +
-                                                   (q - r * cpr) * 8);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kStagePieces; ++i) {
-        const int q = tid + i * kReduceThreads;
-        if (q < pieces)
-            *reinterpret_cast<w4 *>(rows + q * 8) = buf[i];
-    }
-    __syncthreads();
-
     const bool on = lane * V < D;
     uint16_t *lds_row = nrow[wave];
-    for (int st = wave; st * 64 < n; st += kReduceThreads / 64) {
-        const int j = st * 64 + lane;
-        const int kj = j < n ? skey[j] : K;
-        uint64_t starts = __ballot(j < n && kj < K && (j == 0 || skey[j - 1] != kj));
-        while (starts) {
-            const int a = st * 64 + __builtin_ctzll(starts);
-            starts &= starts - 1;
-            const int k = __builtin_amdgcn_readfirstlane(skey[a]);
-            int b = n;
-            for (int base = a + 1; base < n; base += 64) {
-                const int q = base + lane;
-                const uint64_t diff = __ballot(q < n && skey[q] != k);
-                if (diff) {
-                    b = base + __builtin_ctzll(diff);
-                    break;
-                }
-            }
-            float acc[V];
+
+    int kr[kKeysPerThread], vr[kKeysPerThread], er[2] = {-1, -1};
+    auto load_keys = [&](int c) __attribute__((always_inline)) {
+        const int c0 = c * P;
+        const int n = min(N - c0, P);
 #pragma unroll
-            for (int v = 0; v < V; ++v)
-                acc[v] = 0.0f;
-            if (on) {
-                const uint16_t *src = rows + lane * V;
-#pragma unroll 8
-                for (int p = a; p < b; ++p) {
-                    const RowBits<V> r = lds_row_bits<V>(src + p * D);
+        for (int u = 0; u < kKeysPerThread; ++u) {
+            const int j = tid + u * kReduceThreads;
+            kr[u] = j < n ? keys[c0 + j] : 0;
+            vr[u] = j < n ? vals[c0 + j] : 0;
+        }
+        if (tid == 0) {
+            er[0] = c0 > 0 ? keys[c0 - 1] : -1;
+            er[1] = c0 + n < N ? keys[c0 + n] : -1;
+        }
+    };
+    auto store_keys = [&](int b, int c) __attribute__((always_inline)) {
+        const int n = min(N - c * P, P);
 #pragma unroll
-                    for (int v = 0; v < V; ++v)
-                        acc[v] += row_value<V>(r, v);
-                }
-            }
-            const bool before = a == 0 && edge[0] == k;
-            const bool after = b == n && edge[1] == k;
-            if (lane == 0) {
-                if (!before)
-                    start[k] = c0 + a;
-                if (!after)
-                    end[k] = c0 + b;
-            }
-            if (!before && !after) {
-                emit_mean<V>(k, acc, b - a, D, lane, lds_row, C_new, means, norms, counts);
-            } else if (on) {
-                float *dst = partial + (static_cast<size_t>(chunk) * 2 + (before ? 0 : 1)) * D +
-                             lane * V;
-                store_f32<V>(dst, acc);
+        for (int u = 0; u < kKeysPerThread; ++u) {
+            const int j = tid + u * kReduceThreads;
+            if (j < n) {
+                skey[b][j] = kr[u];
+                sval[b][j] = vr[u];
             }
         }
+        if (tid == 0) {
+            edge[b][0] = er[0];
+            edge[b][1] = er[1];
+        }
+    };
+    // 16-byte piece q of a chunk is column (q % cpr) * 8 of its row q / cpr
+    // (q / cpr as (q * cpr_inv) >> 20, exact for q < 4096 and cpr <= 64).
+    // Rows of stray labels are staged too (they are point rows all the
+    // same) and never read.
+    w4 buf[kStagePieces];
+    auto load_rows = [&](int b, int c) __attribute__((always_inline)) {
+        const int pieces = min(N - c * P, P) * cpr;
+#pragma unroll
+        for (int i = 0; i < kStagePieces; ++i) {
+            const int q = tid + i * kReduceThreads;
+            buf[i] = w4{0u, 0u, 0u, 0u};
+            if (q < pieces) {
+                const int r = (q * cpr_inv) >> 20;
+                buf[i] = *reinterpret_cast<const w4 *>(X + static_cast<size_t>(sval[b][r]) * D +
+                                                       (q - r * cpr) * 8);
+            }
+        }
+    };
+    auto store_rows = [&](int c) __attribute__((always_inline)) {
+        const int pieces = min(N - c * P, P) * cpr;
+#pragma unroll
+        for (int i = 0; i < kStagePieces; ++i) {
+            const int q = tid + i * kReduceThreads;
+            if (q < pieces)
+                *reinterpret_cast<w4 *>(rows + q * 8) = buf[i];
+        }
+    };
+
+    int c = blockIdx.x;
+    if (c >= chunks)
+        return;
+    load_keys(c);
+    store_keys(0, c);
+    __syncthreads();
+    if (c + G < chunks)
+        load_keys(c + G);
+    load_rows(0, c);
+    for (int b = 0; c < chunks; c += G, b ^= 1) {
+        const int cn = c + G;
+        store_rows(c);
+        if (cn < chunks)
+            store_keys(b ^ 1, cn);
+        __syncthreads();
+        if (cn + G < chunks)
+            load_keys(cn + G);
+        if (cn < chunks)
+            load_rows(b ^ 1, cn);
+
+        const int c0 = c * P;
+        const int n = min(N - c0, P);
+        const int *sk = skey[b];
+        for (int st = wave; st * 64 < n; st += kReduceThreads / 64) {
+            const int j = st * 64 + lane;
+            const int kj = j < n ? sk[j] : K;
+            uint64_t starts = __ballot(j < n && kj < K && (j == 0 || sk[j - 1] != kj));
+            while (starts) {
+                const int a = st * 64 + __builtin_ctzll(starts);
+                starts &= starts - 1;
+                const int k = __builtin_amdgcn_readfirstlane(sk[a]);
+                int e = n;
+                for (int base = a + 1; base < n; base += 64) {
+                    const int q = base + lane;
+                    const uint64_t diff = __ballot(q < n && sk[q] != k);
+                    if (diff) {
+                        e = base + __builtin_ctzll(diff);
+                        break;
+                    }
+                }
+                float acc[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    acc[v] = 0.0f;
+                if (on) {
+                    const uint16_t *src = rows + lane * V;
+#pragma unroll 8
+                    for (int p = a; p < e; ++p) {
+                        const RowBits<V> r = lds_row_bits<V>(src + p * D);
+#pragma unroll
+                        for (int v = 0; v < V; ++v)
+                            acc[v] += row_value<V>(r, v);
+                    }
+                }
+                const bool before = a == 0 && edge[b][0] == k;
+                const bool after = e == n && edge[b][1] == k;
+                if (lane == 0) {
+                    if (!before)
+                        start[k] = c0 + a;
+                    if (!after)
+                        end[k] = c0 + e;
+                }
+                if (!before && !after) {
+                    emit_mean<V>(k, acc, e - a, D, lane, lds_row, C_new, means, norms, counts);
+                } else if (on) {
+                    float *dst = partial + (static_cast<size_t>(c) * 2 + (before ? 0 : 1)) * D +
+                                 lane * V;
+                    store_f32<V>(dst, acc);
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -632,9 +691,10 @@ hipError_t launch_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *k
     const dim3 block(kReduceThreads);
     if (N > 0) {
         const int cpr_inv = ((1 << 20) + D / 8 - 1) / (D / 8);
-        hipLaunchKernelGGL(upd_reduce_kernel<V>, dim3(pl.chunks), block, 0, stream, X, keys, vals,
-                           N, D, K, pl.chunk, cpr_inv, start, end, partial, C_new, means, norms,
-                           counts);
+        const int wgs = min(pl.chunks, 4 * pl.compute_units);
+        hipLaunchKernelGGL(upd_reduce_kernel<V>, dim3(wgs), block, 0, stream, X, keys, vals, N,
+                           D, K, pl.chunk, pl.chunks, cpr_inv, start, end, partial, C_new, means,
+                           norms, counts);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -647,8 +707,9 @@ hipError_t launch_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *k
 
 }  // namespace
 
-UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K) {
+UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units) {
     UpdatePlan p{};
+    p.compute_units = compute_units > 0 ? compute_units : kDefaultComputeUnits;
     int bits = 0;
     while ((int64_t(1) << bits) <= K)
         ++bits;                                   // keys run 0..K
@@ -752,3 +813,52 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
 }
 
 }  // namespace kmeans
+
+// ---- C entry point ---------------------------------------------------------
+
+extern "C" kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
+                                         int64_t N, int64_t D, int64_t K, void *C_new,
+                                         float *norms, int32_t *counts, float *means,
+                                         hipStream_t stream) {
+    using namespace kmeans;
+    if (N < 0)
+        return fail(KMEANS_ERR_INVALID_ARG, "N=%lld must be >= 0", static_cast<long long>(N));
+    if (K < 1)
+        return fail(KMEANS_ERR_INVALID_ARG, "K=%lld must be >= 1", static_cast<long long>(K));
+    kmeans_status_t st = check_d(D);
+    if (st != KMEANS_OK)
+        return st;
+    if (N > kMaxRows || K > kMaxRows)
+        return fail(KMEANS_ERR_UNSUPPORTED, "N=%lld or K=%lld too large (max %lld)",
+                    static_cast<long long>(N), static_cast<long long>(K),
+                    static_cast<long long>(kMaxRows));
+    if (!C_old || !C_new || !norms || !counts || (N > 0 && (!X || !labels)))
+        return fail(KMEANS_ERR_INVALID_ARG, "null pointer argument (X=%p labels=%p C_old=%p "
+                    "C_new=%p norms=%p counts=%p)", X, static_cast<const void *>(labels), C_old,
+                    C_new, static_cast<void *>(norms), static_cast<void *>(counts));
+    if ((N > 0 && !aligned(X, 16)) || !aligned(C_old, 16) || !aligned(C_new, 16))
+        return fail(KMEANS_ERR_ALIGNMENT, "X, C_old and C_new must be 16-byte aligned");
+    if ((N > 0 && !aligned(labels, 4)) || !aligned(norms, 4) || !aligned(counts, 4) ||
+        !aligned(means, 4))
+        return fail(KMEANS_ERR_ALIGNMENT, "labels, norms, counts and means must be 4-byte aligned");
+
+    const UpdatePlan pl = make_update_plan(N, D, K, device_compute_units());
+    void *ws = nullptr;
+    if (pl.bytes > 0) {
+        hipError_t e = hipMallocAsync(&ws, pl.bytes, stream);
+        if (e != hipSuccess || ws == nullptr)
+            return fail(KMEANS_ERR_NO_MEMORY, "hipMallocAsync(%zu) failed: %s", pl.bytes,
+                        hipGetErrorString(e));
+    }
+    hipError_t e = launch_update(pl, static_cast<const uint16_t *>(X), labels,
+                                         static_cast<const uint16_t *>(C_old),
+                                         static_cast<int>(N), static_cast<int>(D),
+                                         static_cast<int>(K), static_cast<uint16_t *>(C_new),
+                                         norms, counts, means, ws, stream);
+    hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+    if (e != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "update launch failed: %s", hipGetErrorString(e));
+    if (ef != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "hipFreeAsync failed: %s", hipGetErrorString(ef));
+    return ok();
+}

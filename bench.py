@@ -388,13 +388,19 @@ def run_update(args):
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        X0, C0, l0 = host[0]
-        t0 = time.perf_counter()
-        oracle.update(X0, l0, C0)
-        dt = time.perf_counter() - t0
-        cpu = dict(value=N / dt, unit="points/s", cores=1, kind="oracle",
-                   sample=f"the whole workload (seed {W.SEEDS[0]}), fp64, one thread, "
-                          f"{dt:.2f} s wall")
+        # The whole workload takes the oracle well under a second: repeat it
+        # over the three sets until a second has passed.
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            X0, C0, l0 = host[reps % len(host)]
+            oracle.update(X0, l0, C0)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 1.0:
+                break
+        cpu = dict(value=reps * N / dt, unit="points/s", cores=1, kind="oracle",
+                   sample=f"the whole workload, {reps} calls over the three seeded sets, "
+                          f"fp64, one thread, {dt:.2f} s wall")
     out = {
         "metric": UPDATE_METRIC.format(N=N, D=D, K=K),
         "value": N / (ms_per_step / 1e3),

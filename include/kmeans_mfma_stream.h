@@ -2,8 +2,8 @@
  * kmeans_mfma_stream.h -- measurement probe shipped beside the assignment
  * library (libkmeans_mfma_stream.so); not part of the assignment path.
  *
- * A back-to-back stream of the assign kernel's MFMA (bf16 x bf16 -> fp32,
- * 32x32x16) on operands the caller supplies, with no memory traffic or
+ * A back-to-back stream of the assign kernel's MFMA at D = 128 (bf16 x bf16
+ * -> fp32, 16x16x32) on operands the caller supplies, with no memory traffic or
  * epilogue in the loop.  Its flop rate is the ceiling of the matrix pipe for
  * those bit patterns on the running GPU (the part lowers its clock under
  * dense bf16 MFMA with realistic data), against which the assign kernel's
@@ -21,8 +21,9 @@ extern "C" {
 
 /*
  * Launch `workgroups` workgroups of kmeans_mfma_stream_threads() threads
- * (4 waves, 2 waves per SIMD); each wave issues 16 * (1 + 2 * floor(tiles / 2))
- * MFMAs of 32*32*16*2 flop (16 * tiles for odd `tiles`).  Asynchronous on `stream`; time it with events.
+ * (4 waves, 2 waves per SIMD); each wave issues 32 * (1 + 2 * floor(tiles / 2))
+ * MFMAs of 16*16*32*2 flop (32 * tiles for odd `tiles`).  Asynchronous on
+ * `stream`; time it with events.
  *
  *   a_rows, b_rows  bf16 [rows][128], device, 16-byte aligned: the A
  *                   (centroid-like) and B (point-like) operand rows; wave w

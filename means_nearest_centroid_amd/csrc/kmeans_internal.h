@@ -48,6 +48,18 @@ constexpr int assign_wgs_per_cu(int ks) {
 }
 constexpr int kDefaultComputeUnits = 256;   // MI355X
 
+// MFMA geometry of the assign kernel for a padded width of 16*ks: 16 =
+// v_mfma_f32_16x16x32_bf16, 32 = v_mfma_f32_32x32x16_bf16.  Back to back on
+// realistic bf16 data the 16x16x32 form sustains about 10% more on MI355X
+// (it reads half the accumulator registers per flop), and its half-size
+// accumulators leave room for reduction rotation at D >= 256; at D <= 64 a
+// 16x16x32 point block holds only two k-steps, too little matrix time to
+// hide its reduction behind, so the 32x32x16 form stays there; at D = 512
+// two 16x16x32 point blocks of 16 k-steps spill, and one 32x32x16 block
+// does not.  Every path of one D uses the same form, so their outputs stay
+// bitwise identical.
+constexpr int mfma_geometry(int ks) { return ks == 8 || ks == 16 ? 16 : 32; }
+
 struct Plan {
     int path;          // 1 direct, 2 split (as kmeans_path_t)
     int splits;        // K-ranges (grid.y)

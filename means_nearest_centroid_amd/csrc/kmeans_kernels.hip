@@ -6,9 +6,12 @@
 // minimum.  Design for CDNA4, not a translation of the pages' Blackwell
 // kernel:
 //
-//  * The x.c contraction runs on bf16 MFMA (v_mfma_f32_32x32x16_bf16): the
-//    centroid tile is the A operand (32 rows), 32 points are the B operand.
-//    Each lane then owns 16 scores of ONE point, so the argmin needs no
+//  * The x.c contraction runs on bf16 MFMA: the centroid tile (32 rows) is
+//    the A operand, the points the B operand.  At D = 128 and 256 it is
+//    v_mfma_f32_16x16x32_bf16 on two 16-row A blocks and 16-point B blocks
+//    (8 scores per lane per point block), elsewhere v_mfma_f32_32x32x16_bf16
+//    on one 32-row A block and 32-point B blocks (16 scores per lane).  Each
+//    lane owns scores of ONE point per block, so the argmin needs no
 //    cross-lane traffic inside the hot loop.
 //  * The norm is folded into the accumulator: the points are held as -2x
 //    (exact in bf16) and the MFMA's C input is the norm tile, so the MFMA
@@ -17,7 +20,7 @@
 //    norms" / "Barrier elimination" rows reach the same goal on Blackwell).
 //  * Points stay resident in VGPRs for the whole K loop; centroid blocks are
 //    double-buffered through LDS with an XOR swizzle so the A-operand reads
-//    (ds_read_b128, 32 rows at one column) hit distinct banks.  Buffer loads
+//    (ds_read_b128, 16 or 32 rows at one column) hit distinct banks.  Buffer loads
 //    return zero past the end, so ragged N, K and D need no branches.
 //  * Reductions never wait on the matrix pipe: a point block's scores are
 //    reduced only after the MFMAs of the next point block (or tile) have
@@ -193,7 +196,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, KM_LDS void *dst
 //       best = m, best_tile = tile, best_slot = slot
 // m is always one of its inputs, so the winner is exact; a strict '<' keeps
 // the earlier tile on equal scores, and the slot search keeps the lower row.
-template <int KS, int P, int BK, int WAVES, int WPE>
+template <int G, int KS, int P, int BK, int WAVES, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
@@ -201,6 +204,21 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                    int write_partials, int32_t *__restrict__ labels,
                    float *__restrict__ min_dist, float *__restrict__ ws_score,
                    int32_t *__restrict__ ws_label, float *__restrict__ ws_xx) {
+    // MFMA geometry.  G = 32: v_mfma_f32_32x32x16_bf16, one 32-row A block
+    // per tile, 32-point B blocks, k-steps of 16; lane = (pcol = lane % 32,
+    // kq = lane / 32); accumulator element e is tile row 8(e/4) + 4kq + e%4.
+    // G = 16: v_mfma_f32_16x16x32_bf16, two 16-row A blocks per tile, each
+    // 32-point block split into two 16-point B blocks, k-steps of 32; lane =
+    // (pcol = lane % 16, kq = lane / 16); element e of A block m is tile row
+    // 16m + 4kq + e.  Either way a lane holds scores of one point only, and
+    // the 64 / G lanes with the same pcol share that point.
+    constexpr int KSTEP = G == 32 ? 16 : 32;
+    constexpr int NKS = KS * 16 / KSTEP;       // MFMA k-steps over the padded row
+    static_assert(NKS >= 1 && NKS * KSTEP == KS * 16, "padded D must cover whole k-steps");
+    constexpr int MB = 32 / G;                 // A row blocks per 32-row tile
+    constexpr int PB = P * (32 / G);           // B point blocks per wave
+    constexpr int AV = G * G / 64;             // accumulator floats per lane per MFMA
+    typedef float accv __attribute__((ext_vector_type(AV)));
     constexpr int S = 2 * KS;                  // 16-byte chunks per centroid row
     constexpr int ROW_BYTES = 16 * S;
     constexpr int TB = BK / kTileRows;         // tiles per block
@@ -217,8 +235,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int col = lane & 31;   // point column of the B tile; row of the A tile
-    const int half = lane >> 5;  // which 8-element half of a 16-wide k-step
+    const int pcol = lane % G;   // point column of a B block; row of an A block
+    const int kq = lane / G;     // which 8-element group of a k-step
 
     const int split = blockIdx.y;
     const int k_begin = split * k_chunk;
@@ -227,8 +245,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     const int wg_points = min(N - wg_point0, WAVES * P * kTileCols);
     const uint32_t row_bytes = static_cast<uint32_t>(D) * 2u;
 
-    u32x4 xb[P][KS];     // resident points (-2x), loaded below
-    float xx[P];
+    u32x4 xb[PB][NKS];   // resident points (-2x), loaded below
+    float xx[PB];
 
     // ---- centroid blocks: DMA into the LDS ring, norms via one register ----
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(C + static_cast<size_t>(k_begin) * D,
@@ -267,53 +285,68 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     };
 
     // Per-lane LDS read offsets inside a tile (tiles start at multiples of 32
-    // rows, where the swizzle pattern repeats).
-    int a_off[KS];
+    // rows, where the swizzle pattern repeats): A block m, k-step ks.
+    int a_off[MB][NKS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        a_off[ks] = col * ROW_BYTES + swz<S>(col, 2 * ks + half) * 16;
-    auto read_a = [&](const uint8_t *stage, int r0, int ks) KM_INLINE {
+    for (int m = 0; m < MB; ++m) {
+        const int row = m * G + pcol;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            a_off[m][ks] = row * ROW_BYTES + swz<S>(row, ks * (KSTEP / 8) + kq) * 16;
+    }
+    auto read_a = [&](const uint8_t *stage, int r0, int m, int ks) KM_INLINE {
         return __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4 *>(&stage[r0 * ROW_BYTES + a_off[ks]]));
+            bf16x8, *reinterpret_cast<const u32x4 *>(&stage[r0 * ROW_BYTES + a_off[m][ks]]));
     };
-    // Norm tile as the MFMA C input: slot r of this lane is tile row
-    // 8*(r/4) + 4*half + r%4.
-    auto read_n = [&](const float *stage, int r0) KM_INLINE {
-        f32x16 v;
+    // Norm tile as the MFMA C input, element e of A block m at its tile row.
+    auto read_n = [&](const float *stage, int r0, accv (&v)[MB]) KM_INLINE {
+        if constexpr (G == 32) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(&stage[r0 + 8 * q + 4 * half]);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(&stage[r0 + 8 * q + 4 * kq]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[4 * q + e] = t[e];
+                for (int e = 0; e < 4; ++e)
+                    v[0][4 * q + e] = t[e];
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+                v[m] = *reinterpret_cast<const f32x4 *>(&stage[r0 + 16 * m + 4 * kq]);
         }
-        return v;
+    };
+    // Tile row of element e of A block m, less this lane's 4*kq.
+    auto row_of = [](int m, int e) constexpr {
+        return G == 32 ? 8 * (e >> 2) + (e & 3) : 16 * m + e;
     };
 
-    bf16x8 a[KS];
-    f32x16 ninit;
+    bf16x8 a[MB][NKS];
+    accv ninit[MB];
 
-    float bs[P];
-    int32_t bt[P], bo[P];
+    float bs[PB];
+    int32_t bt[PB], bo[PB];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < PB; ++p) {
         bs[p] = INFINITY;
         bt[p] = kNoLabel;
         bo[p] = 0;
     }
-    // Fold the 16 scores of point block p in v (centroids kt + 8*(r/4) +
-    // 4*half + r%4) into that block's running best.
-    auto reduce = [&](int p, const f32x16 &v, int kt) KM_INLINE {
-        float m = bs[p];
+    // Fold the scores of point block p in v (centroid kt + row_of(m, e) +
+    // 4*kq) into that block's running best.
+    auto reduce = [&](int p, const accv (&v)[MB], int kt) KM_INLINE {
+        float mn = bs[p];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2)
-            m = __builtin_fminf(__builtin_fminf(m, v[r]), v[r + 1]);
-        if (m < bs[p]) {
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < AV; r += 2)
+                mn = __builtin_fminf(__builtin_fminf(mn, v[m][r]), v[m][r + 1]);
+        if (mn < bs[p]) {
             int slot = 0;
 #pragma unroll
-            for (int r = 15; r >= 0; --r)
-                slot = v[r] == m ? 8 * (r >> 2) + (r & 3) : slot;
-            bs[p] = m;
+            for (int m = MB - 1; m >= 0; --m)
+#pragma unroll
+                for (int r = AV - 1; r >= 0; --r)
+                    slot = v[m][r] == mn ? row_of(m, r) : slot;
+            bs[p] = mn;
             bt[p] = kt;
             bo[p] = slot;
         }
@@ -325,41 +358,53 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     // after the first block of this tile).  With one block per wave, two
     // accumulator sets alternate between tiles and the previous tile is
     // reduced while this one's MFMAs run.  The set read first holds +inf.
-    // At D >= 256 the second set does not fit the register budget: a tile is
-    // reduced right after its own MFMAs and the other wave of the SIMD keeps
-    // the matrix pipe busy meanwhile.
-    constexpr int NACC = P > 1 ? P : (KS <= 8 ? 2 : 1);
-    static_assert(NACC != 2 || P > 1 || TB % 2 == 0, "tile parity must repeat in every block");
-    f32x16 acc[NACC];
+    // At D >= 256 with G = 32 the second set does not fit the register
+    // budget: a tile is reduced right after its own MFMAs and the other wave
+    // of the SIMD keeps the matrix pipe busy meanwhile.
+    constexpr int NACC = PB > 1 ? PB : (KS <= 8 ? 2 : 1);
+    static_assert(NACC != 2 || PB > 1 || TB % 2 == 0, "tile parity must repeat in every block");
+    accv acc[NACC][MB];
     if (NACC > 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            acc[NACC - 1][r] = INFINITY;
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < AV; ++r)
+                acc[NACC - 1][m][r] = INFINITY;
     }
+    auto mfma = [](const bf16x8 &x, const bf16x8 &y, const accv &c) KM_INLINE {
+        if constexpr (G == 32)
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+    };
     // One tile (j-th of its block, first centroid kt): MFMAs with the
     // current operands (a, ninit), whose registers are refilled with the next
     // tile's fragments right after their last use, interleaved with the
     // reductions.
     auto tile = [&](const uint8_t *next_c, const float *next_n, int next_r0, int kt, int j) KM_INLINE {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            f32x16 &dst = acc[P > 1 ? p : (NACC == 2 ? (j & 1) : 0)];
+        for (int p = 0; p < PB; ++p) {
+            accv (&dst)[MB] = acc[PB > 1 ? p : (NACC == 2 ? (j & 1) : 0)];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                dst = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    a[ks], __builtin_bit_cast(bf16x8, xb[p][ks]), ks == 0 ? ninit : dst, 0, 0, 0);
-                if (p == P - 1) {
-                    a[ks] = read_a(next_c, next_r0, ks);
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+                    dst[m] = mfma(a[m][ks], __builtin_bit_cast(bf16x8, xb[p][ks]),
+                                  ks == 0 ? ninit[m] : dst[m]);
+                if (p == PB - 1) {
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+                        a[m][ks] = read_a(next_c, next_r0, m, ks);
                     if (ks == 0)
-                        ninit = read_n(next_n, next_r0);
+                        read_n(next_n, next_r0, ninit);
                 }
             }
             if (NACC == 1)
                 reduce(0, acc[0], kt);
-            else if (P == 1)
+            else if (PB == 1)
                 reduce(0, acc[(j + 1) & 1], kt - kTileRows);
             else if (p == 0)
-                reduce(P - 1, acc[P - 1], kt - kTileRows);
+                reduce(PB - 1, acc[PB - 1], kt - kTileRows);
             else
                 reduce(p - 1, acc[p - 1], kt);
         }
@@ -375,11 +420,11 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + static_cast<size_t>(wg_point0) * D,
                                                 static_cast<uint32_t>(wg_points) * row_bytes);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const uint32_t prow = static_cast<uint32_t>((wave * P + p) * kTileCols + col);
+    for (int p = 0; p < PB; ++p) {
+        const uint32_t prow = static_cast<uint32_t>(wave * P * kTileCols + p * G + pcol);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c0 = ks * 16 + half * 8;
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = ks * KSTEP + kq * 8;
             xb[p][ks] = load16(xr, c0 < D ? prow * row_bytes + c0 * 2 : kOutOfRange);
         }
     }
@@ -387,12 +432,14 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     // waits would also wait for block 0's DMA (loads complete in order).
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < PB; ++p) {
         xx[p] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
             xb[p][ks] = neg2_and_square(xb[p][ks], xx[p]);
-        xx[p] += __shfl_xor(xx[p], 32);
+#pragma unroll
+        for (int off = G; off < 64; off <<= 1)
+            xx[p] += __shfl_xor(xx[p], off);
     }
 
     wait_vmem();      // block 0, its norms and the points, in one round trip
@@ -404,9 +451,11 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         load_norm(1);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        a[ks] = read_a(c_st0, 0, ks);
-    ninit = read_n(n_st0, 0);
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            a[m][ks] = read_a(c_st0, 0, m, ks);
+    read_n(n_st0, 0, ninit);
 
     // Block b lives in stage cc/nc, block b+1 in cn/nn; block b+2 is fetched
     // into cc/nc once the barrier shows nobody reads block b any more.
@@ -437,22 +486,25 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         do_block(b + 1, c_st1, n_st1, c_st0, n_st0);
     }
     if (NACC > 1)   // the last tile's last point block
-        reduce(P - 1, acc[P > 1 ? P - 1 : ((TB - 1) & 1)],
+        reduce(PB - 1, acc[PB > 1 ? PB - 1 : ((TB - 1) & 1)],
                k_begin + (nblocks - 1) * BK + (TB - 1) * kTileRows);
 
-    // ---- merge the two lanes that hold the same point ----
+    // ---- merge the lanes that hold the same point ----
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < PB; ++p) {
         float s = bs[p];
-        int32_t i = bt[p] == kNoLabel ? kNoLabel : bt[p] + bo[p] + 4 * half;
-        const float so = __shfl_xor(s, 32);
-        const int32_t io = __shfl_xor(i, 32);
-        if (pair_before(so, io, s, i)) {
-            s = so;
-            i = io;
+        int32_t i = bt[p] == kNoLabel ? kNoLabel : bt[p] + bo[p] + 4 * kq;
+#pragma unroll
+        for (int off = G; off < 64; off <<= 1) {
+            const float so = __shfl_xor(s, off);
+            const int32_t io = __shfl_xor(i, off);
+            if (pair_before(so, io, s, i)) {
+                s = so;
+                i = io;
+            }
         }
-        const int n = wg_point0 + (wave * P + p) * kTileCols + col;
-        if (half == 0 && n < N) {
+        const int n = wg_point0 + wave * P * kTileCols + p * G + pcol;
+        if (kq == 0 && n < N) {
             if (write_partials) {
                 ws_score[static_cast<size_t>(split) * N + n] = s;
                 ws_label[static_cast<size_t>(split) * N + n] = i;
@@ -511,7 +563,7 @@ hipError_t launch_assign_kp(const Plan &pl, const uint16_t *X, const uint16_t *C
     constexpr int WPE = waves_per_simd(KS);
     static_assert(assign_wgs_per_cu(KS) >= 1, "workgroup must fit a CU");
     const int partial = ws_score != nullptr ? 1 : 0;
-    hipLaunchKernelGGL((assign_kernel<KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
+    hipLaunchKernelGGL((assign_kernel<mfma_geometry(KS), KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
                        0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, labels, min_dist,
                        ws_score, ws_label, ws_xx);
     return hipGetLastError();

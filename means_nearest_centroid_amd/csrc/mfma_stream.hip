@@ -1,11 +1,11 @@
 // mfma_stream.hip -- measurement probe, not part of the assignment path.
 //
-// Runs the assign kernel's matrix instruction (v_mfma_f32_32x32x16_bf16,
-// fp32 accumulate) back to back with nothing else in the loop: no LDS, no
-// VALU epilogue, no global traffic.  Each wave holds one 32-row A operand
-// and two 32-column B operands of D = 128 (the headline shape's tile) in
-// VGPRs and issues 16 MFMAs per tile in two chains that restart from a
-// fixed C tile every tile, as the assign kernel's do.  Two waves per SIMD.
+// Runs the assign kernel's matrix instruction at the headline width D = 128
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulate) back to back with nothing else
+// in the loop: no LDS, no VALU epilogue, no global traffic.  Each wave holds
+// two 16-row A blocks and four 16-column B blocks of D = 128 in VGPRs and
+// issues 32 MFMAs per tile in eight chains that restart from a fixed C tile
+// every tile, as the assign kernel's do.  Two waves per SIMD.
 //
 // The rate it reaches is the ceiling of the matrix pipe for those operand
 // bit patterns on the running part: with zero operands it is close to the
@@ -18,11 +18,11 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;          // columns of every operand row
-constexpr int kKs = kD / 16;     // k-steps per tile
+constexpr int kKs = kD / 32;     // k-steps per tile
 constexpr int kThreads = 256;    // 4 waves
 
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
@@ -31,52 +31,64 @@ void mfma_stream_kernel(const uint16_t *__restrict__ a_rows, const uint16_t *__r
                         int rows, int tiles, float *__restrict__ sink) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int col = lane & 31, half = lane >> 5;
+    const int r16 = lane & 15, quad = lane >> 4;
     const int w = blockIdx.x * (kThreads / 64) + wave;
 
-    // Operand fragments: A row = lane % 32, B column = lane % 32, k-steps
-    // of 16 with this lane's 8-element half.  Rows wrap inside [0, rows).
-    bf16x8 a[kKs], b[2][kKs];
-    const int ar = (w * 32 + col) % rows;
+    // Operand fragments: A row = 16m + lane % 16, B column = 16n + lane % 16,
+    // k-steps of 32 with this lane's 8-element quarter.  Rows wrap inside
+    // [0, rows).
+    bf16x8 a[2][kKs], b[4][kKs];
 #pragma unroll
-    for (int k = 0; k < kKs; ++k)
-        a[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                              a_rows + static_cast<size_t>(ar) * kD + k * 16 + half * 8));
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int br = (w * 64 + p * 32 + col) % rows;
+    for (int m = 0; m < 2; ++m) {
+        const int ar = (w * 32 + m * 16 + r16) % rows;
 #pragma unroll
         for (int k = 0; k < kKs; ++k)
-            b[p][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                                     b_rows + static_cast<size_t>(br) * kD + k * 16 + half * 8));
+            a[m][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                                     a_rows + static_cast<size_t>(ar) * kD + k * 32 + quad * 8));
     }
-    f32x16 c0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-        c0[r] = static_cast<float>(r + 8 * half);
+    for (int n = 0; n < 4; ++n) {
+        const int br = (w * 64 + n * 16 + r16) % rows;
+#pragma unroll
+        for (int k = 0; k < kKs; ++k)
+            b[n][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                                     b_rows + static_cast<size_t>(br) * kD + k * 32 + quad * 8));
+    }
+    f32x4 c0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        c0[r] = static_cast<float>(r + 4 * quad);
     // Two accumulator sets: while one tile's chains run, the previous tile's
-    // results are read (one VALU op per 8 MFMAs), so no read waits on an
-    // MFMA in flight.
-    f32x16 acc[2][2];
-    auto tile = [&](f32x16 (&out)[2]) {
+    // results are read (one VALU op per 4 MFMAs), so no read waits on an MFMA
+    // in flight.  Every chain is read, so none is optimised away.
+    f32x4 acc[2][8];
+    auto tile = [&](f32x4 (&out)[8]) {
         c0[0] += 0.5f;   // a different C tile each time, as the assign kernel's norm tiles
 #pragma unroll
         for (int k = 0; k < kKs; ++k) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
-                out[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[p][k], k == 0 ? c0 : out[p],
-                                                                 0, 0, 0);
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+                    out[m * 4 + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a[m][k], b[n][k], k == 0 ? c0 : out[m * 4 + n], 0, 0, 0);
         }
     };
     float keep = 0.0f;
     tile(acc[0]);
     for (int t = 1; t < tiles; t += 2) {
         tile(acc[1]);
-        keep += acc[0][0][3] + acc[0][1][11];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            keep += acc[0][j][1 + j % 3];
         tile(acc[0]);
-        keep += acc[1][0][5] + acc[1][1][13];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            keep += acc[1][j][1 + (j + 1) % 3];
     }
-    keep += acc[0][0][1] + acc[0][1][9];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        keep += acc[0][j][1 + (j + 2) % 3];
     sink[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = keep;
 }
 

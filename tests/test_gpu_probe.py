@@ -45,16 +45,17 @@ def test_probe_runs_and_is_deterministic(probe):
 
 def test_probe_zero_operands_give_the_c_tile_sums(probe):
     # With A = B = 0 every MFMA result is its C tile, whose element r in lane
-    # half h is r + 8h (element 0, never read, changes per tile).  The probe
-    # reads elements 3, 11, 5, 13 of the two accumulator sets once per pair
-    # of tiles and elements 1, 9 at the end, so each lane's sink value is
-    # floor(tiles / 2) * (32 + 32h) + 10 + 16h, exactly.
+    # quarter q (lane // 16) is r + 4q (element 0, never read, changes per
+    # tile).  Per pair of tiles the probe reads elements 1 + j % 3 of the
+    # eight chains of one set and 1 + (j + 1) % 3 of the other, and at the
+    # end 1 + (j + 2) % 3: each lane's sink value is floor(tiles / 2) *
+    # (32 + 64q) + 16 + 32q, exactly.
     z = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
     for tiles in (1, 2, 5):
         st, s = run(probe, z, z, 64, tiles, 2)
         assert st == 0
-        h = (np.arange(s.size) % 64) // 32
-        exp = (tiles // 2) * (32.0 + 32.0 * h) + 10.0 + 16.0 * h
+        q = (np.arange(s.size) % 64) // 16
+        exp = (tiles // 2) * (32.0 + 64.0 * q) + 16.0 + 32.0 * q
         assert np.array_equal(s, exp.astype(np.float32)), tiles
 
 

@@ -22,16 +22,17 @@
 //     the rank among equal digits inside a wave, and a per-wave count table
 //     in LDS, tagged with the round so it never needs clearing, the rank
 //     across the tile's waves.
-//  2. The reduce kernel gives each workgroup a fixed chunk of sorted
-//     positions (32 KiB of rows: 128 at D = 128).  It first stages the
-//     chunk's rows in LDS with all row loads in flight at once (a gather of
-//     whole rows, 16 bytes per load), then its waves sum each run of equal
-//     labels from LDS in position order (64 lanes share a row, V bf16 values
-//     each).  A cluster that starts and ends inside the chunk is finished
-//     there; a run cut by a chunk boundary leaves its partial sum, and the
-//     finish kernel adds a cluster's partials in chunk order.  Work per
-//     workgroup is bounded by the chunk, whatever the cluster sizes, and the
-//     order of every sum is fixed by the sorted order.
+//  2. The reduce kernel walks fixed chunks of sorted positions (32 KiB of
+//     rows: 128 at D = 128), four persistent workgroups per CU.  A chunk's
+//     rows are staged in LDS with all its row loads in flight at once (a
+//     gather of whole rows, 16 bytes per load) while the previous chunk is
+//     summed; waves sum each run of equal labels from LDS in position order
+//     (the lanes share a row, V = 2, 4 or 8 bf16 values each).  A cluster
+//     that starts and ends inside the chunk is finished there; a run cut by
+//     a chunk boundary leaves its partial sum, and the finish kernel adds a
+//     cluster's partials in chunk order.  Work per chunk is bounded whatever
+//     the cluster sizes, and the order of every sum is fixed by the sorted
+//     order.
 //  3. Finishing a cluster: mean = sum / count in fp32, rounded to bf16, and
 //     the squared norm of the rounded row computed exactly as the norms
 //     pre-pass computes it (row_sq_norm16 over a copy of the row in LDS).
@@ -42,7 +43,7 @@
 namespace kmeans {
 namespace {
 
-constexpr int kSortThreads = 256;    // 4 waves; one key per thread per round
+constexpr int kSortThreads = 256;    // histogram workgroups: 4 waves
 constexpr int kRadix = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kFusedScanTiles = 128;  // up to this many sort tiles, no scan kernel
@@ -334,15 +335,14 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
 // V bf16 values of one row per lane (lane l holds columns l*V .. l*V+V-1).
 template <int V>
 struct RowBits {
-    uint32_t w[(V + 1) / 2];
+    static_assert(V == 2 || V == 4 || V == 8, "two, four or eight columns per lane");
+    uint32_t w[V / 2];
 };
 
 template <int V>
 __device__ __forceinline__ RowBits<V> load_row(const uint16_t *p) {
     RowBits<V> r;
-    if constexpr (V == 1) {
-        r.w[0] = *p;
-    } else if constexpr (V == 2) {
+    if constexpr (V == 2) {
         r.w[0] = *reinterpret_cast<const uint32_t *>(p);
     } else if constexpr (V == 4) {
         typedef uint32_t w2 __attribute__((ext_vector_type(2)));
@@ -362,17 +362,12 @@ __device__ __forceinline__ RowBits<V> load_row(const uint16_t *p) {
 
 template <int V>
 __device__ __forceinline__ float row_value(const RowBits<V> &r, int v) {
-    if constexpr (V == 1)
-        return widen(r.w[0]);
-    else
-        return (v & 1) ? __uint_as_float(r.w[v >> 1] & 0xffff0000u) : widen(r.w[v >> 1] & 0xffffu);
+    return (v & 1) ? __uint_as_float(r.w[v >> 1] & 0xffff0000u) : widen(r.w[v >> 1] & 0xffffu);
 }
 
 template <int V>
 __device__ __forceinline__ void store_bits(uint16_t *p, const uint32_t (&b)[V]) {
-    if constexpr (V == 1) {
-        *p = static_cast<uint16_t>(b[0]);
-    } else if constexpr (V == 2) {
+    if constexpr (V == 2) {
         *reinterpret_cast<uint32_t *>(p) = b[0] | (b[1] << 16);
     } else if constexpr (V == 4) {
         typedef uint32_t w2 __attribute__((ext_vector_type(2)));
@@ -440,9 +435,7 @@ __device__ __forceinline__ void emit_mean(int k, const float (&sum)[V], int coun
 template <int V>
 __device__ __forceinline__ RowBits<V> lds_row_bits(const uint16_t *p) {
     RowBits<V> r;
-    if constexpr (V == 1) {
-        r.w[0] = *p;
-    } else if constexpr (V == 2) {
+    if constexpr (V == 2) {
         r.w[0] = *reinterpret_cast<const uint32_t *>(p);
     } else if constexpr (V == 4) {
         typedef uint32_t w2 __attribute__((ext_vector_type(2)));

@@ -220,23 +220,27 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
     const int beg = t << tile_log2;
     const int fin = static_cast<int>(min(static_cast<int64_t>(N),
                                          static_cast<int64_t>(beg) + (int64_t(1) << tile_log2)));
+    // Positions inside the tile are counted from beg (at most 2^19 plus a
+    // batch), so that no index past the tile can wrap around 2^31.
+    const int len = fin - beg;
     // Keys and values are loaded kBatchRounds rounds at a time, all loads of
     // a batch in flight together; the first batch is issued before the
     // offsets are worked out, so the two sets of loads overlap.
     int bkey[kBatchRounds], bval[kBatchRounds];
-    auto load_batch = [&](int base0) __attribute__((always_inline)) {
+    auto load_batch = [&](int rel0) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < kBatchRounds; ++r) {
-            const int i = base0 + r * kScatterThreads + tid;
+            const int rel = rel0 + r * kScatterThreads + tid;
             bkey[r] = 0;
             bval[r] = 0;
-            if (i < fin) {
+            if (rel < len) {
+                const int i = beg + rel;
                 bkey[r] = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
                 bval[r] = FIRST ? i : vals_in[i];
             }
         }
     };
-    load_batch(beg);
+    load_batch(0);
     const bool owner = tid < kRadix;       // thread d < 256 owns digit d
     int run = 0;                           // owner: next position of its digit
     if (SCANNED) {
@@ -293,16 +297,16 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
     __syncthreads();
     const uint64_t below = (uint64_t(1) << lane) - 1;
     int tag = 0;
-    for (int base0 = beg; base0 < fin; base0 += kBatchRounds * kScatterThreads) {
-        if (base0 != beg)
-            load_batch(base0);
+    for (int rel0 = 0; rel0 < len; rel0 += kBatchRounds * kScatterThreads) {
+        if (rel0 != 0)
+            load_batch(rel0);
 #pragma unroll
         for (int r = 0; r < kBatchRounds; ++r) {
-            const int base = base0 + r * kScatterThreads;
-            if (base >= fin)
+            const int base = rel0 + r * kScatterThreads;
+            if (base >= len)
                 break;                         // uniform: the tile ends here
             ++tag;
-            const bool valid = base + tid < fin;
+            const bool valid = base + tid < len;
             const int key = bkey[r];
             const int d = (key >> shift) & (kRadix - 1);
             uint64_t same = __ballot(valid);
@@ -641,8 +645,11 @@ void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__rest
     const int lane = threadIdx.x & 63;
     const bool on = lane * V < D;
     uint16_t *lds_row = nrow[wave];
-    const int nwaves = gridDim.x * (kReduceThreads / 64);
-    for (int k = blockIdx.x * (kReduceThreads / 64) + wave; k < K; k += nwaves) {
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kReduceThreads / 64);
+    // 64-bit stride: K may lie within one stride of 2^31.
+    for (int64_t kk = static_cast<int64_t>(blockIdx.x) * (kReduceThreads / 64) + wave; kk < K;
+         kk += nwaves) {
+        const int k = static_cast<int>(kk);
         const int s = N > 0 ? start[k] : 0;
         const int e = N > 0 ? end[k] : 0;
         const int count = e - s;

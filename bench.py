@@ -243,11 +243,16 @@ def settle(step, ms: float):
     return n
 
 
-def mfma_ceiling(X, C, dev, cus: int, tiles: int = 2000, reps: int = 3):
+def mfma_ceiling(X, C, dev, cus: int, tiles: int = 401, launches: int = 30,
+                 settle_ms: float = 250.0):
     """Rate of the MFMA-only probe (libkmeans_mfma_stream.so) on operand rows
     made of this workload's values (points scaled by -2, as the assign kernel
     holds them, and centroids), and on zero operands: the matrix pipe's
-    ceiling for this data on this GPU."""
+    ceiling for this data on this GPU.  Measured the way the assign kernel
+    is: ``settle_ms`` of untimed launches first (the clock a GPU holds under
+    dense MFMA is reached only after some milliseconds), then ``launches``
+    back-to-back launches of about the assign kernel's duration between two
+    events."""
     import ctypes
     import torch
     from means_nearest_centroid_amd import build as kbuild
@@ -269,26 +274,28 @@ def mfma_ceiling(X, C, dev, cus: int, tiles: int = 2000, reps: int = 3):
     flop = 2.0 * 32 * 32 * 16 * 16 * tiles * wgs * (threads // 64)
 
     def rate(a, b):
-        ts = []
-        for r in range(reps + 1):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+        def launch(_i=0):
             st = lib.kmeans_mfma_stream(a.data_ptr(), b.data_ptr(), rows, tiles, wgs,
                                         sink.data_ptr(), stream.cuda_stream)
-            e1.record(stream)
             if st != 0:
                 raise RuntimeError(f"kmeans_mfma_stream failed ({st})")
-            e1.synchronize()
-            if r:
-                ts.append(e0.elapsed_time(e1) / 1e3)
-        return flop / float(np.median(ts)) / 1e12
+        settle(launch, settle_ms)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            launch()
+        e1.record(stream)
+        e1.synchronize()
+        return flop * launches / (e0.elapsed_time(e1) / 1e3) / 1e12
 
     data = rate(operand(C, 1.0), operand(X, -2.0))
     z = torch.zeros((rows, 128), dtype=torch.bfloat16, device=dev)
     zero = rate(z, z)
     return dict(probe="kmeans_mfma_stream: the assign kernel's MFMA back to back, no LDS, "
                       "no epilogue; operands = this workload's rows (x scaled by -2, centroids)",
+                timing=f"{settle_ms:g} ms untimed, then {launches} back-to-back launches "
+                       f"of {tiles} tiles between two events",
                 tflops=round(data, 1), frac_of_peak=round(data / BF16_DENSE_PEAK_TFLOPS, 4),
                 zero_operand_tflops=round(zero, 1))
 

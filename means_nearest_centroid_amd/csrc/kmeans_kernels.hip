@@ -169,6 +169,94 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, KM_LDS void *dst
 #endif
 }
 
+// Lowest row, among the rows one lane holds in a tile, whose score equals m
+// (the minimum of those scores).  v_cmp_eq_f32 treats -0 and +0 as equal,
+// as '==' does.  Written as assembly so that compares and selects alternate
+// through three rotating SGPR pairs, each select two instructions behind the
+// compare it reads: the compiler's form sends every compare through VCC and
+// must wait two cycles before each select, a serial chain with a stall per
+// score.  Runs only on lanes whose best improved (under the exec mask of
+// the caller's branch).
+//
+// 16x16x32 layout: scores a[0..3] are tile rows 0..3 and b[0..3] rows
+// 16..19 (plus the lane's 4 * (lane / 16), added by the caller).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ int lowest_row_of_min_16x16(const f32x4 &a, const f32x4 &b, float m) {
+    int row = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint64_t ka, kb, kc;
+    asm volatile(
+        "v_cmp_eq_f32_e64 %[ka], %[b3], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[b2], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[kc], %[b1], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], 0, 19, %[ka]\n\t"
+        "v_cmp_eq_f32_e64 %[ka], %[b0], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 18, %[kb]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[a3], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 17, %[kc]\n\t"
+        "v_cmp_eq_f32_e64 %[kc], %[a2], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 16, %[ka]\n\t"
+        "v_cmp_eq_f32_e64 %[ka], %[a1], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 3, %[kb]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[a0], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 2, %[kc]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 1, %[ka]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 0, %[kb]"
+        : [row] "=&v"(row), [ka] "=&s"(ka), [kb] "=&s"(kb), [kc] "=&s"(kc)
+        : [m] "v"(m), [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]),
+          [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]));
+#endif
+    return row;
+}
+
+// 32x32x16 layout: score e (0..15) is tile row 8 * (e / 4) + e % 4 (plus the
+// lane's 4 * (lane / 32)).
+__device__ __forceinline__ int lowest_row_of_min_32x32(const f32x16 &s, float m) {
+    int row = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint64_t ka, kb, kc;
+    asm volatile(
+        "v_cmp_eq_f32_e64 %[ka], %[s15], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[s14], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[kc], %[s13], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], 0, 27, %[ka]\n\t"
+        "v_cmp_eq_f32_e64 %[ka], %[s12], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 26, %[kb]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[s11], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 25, %[kc]\n\t"
+        "v_cmp_eq_f32_e64 %[kc], %[s10], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 24, %[ka]\n\t"
+        "v_cmp_eq_f32_e64 %[ka], %[s9], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 19, %[kb]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[s8], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 18, %[kc]\n\t"
+        "v_cmp_eq_f32_e64 %[kc], %[s7], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 17, %[ka]\n\t"
+        "v_cmp_eq_f32_e64 %[ka], %[s6], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 16, %[kb]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[s5], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 11, %[kc]\n\t"
+        "v_cmp_eq_f32_e64 %[kc], %[s4], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 10, %[ka]\n\t"
+        "v_cmp_eq_f32_e64 %[ka], %[s3], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 9, %[kb]\n\t"
+        "v_cmp_eq_f32_e64 %[kb], %[s2], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 8, %[kc]\n\t"
+        "v_cmp_eq_f32_e64 %[kc], %[s1], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 3, %[ka]\n\t"
+        "v_cmp_eq_f32_e64 %[ka], %[s0], %[m]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 2, %[kb]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 1, %[kc]\n\t"
+        "v_cndmask_b32_e64 %[row], %[row], 0, %[ka]"
+        : [row] "=&v"(row), [ka] "=&s"(ka), [kb] "=&s"(kb), [kc] "=&s"(kc)
+        : [m] "v"(m), [s0] "v"(s[0]), [s1] "v"(s[1]), [s2] "v"(s[2]), [s3] "v"(s[3]),
+          [s4] "v"(s[4]), [s5] "v"(s[5]), [s6] "v"(s[6]), [s7] "v"(s[7]), [s8] "v"(s[8]),
+          [s9] "v"(s[9]), [s10] "v"(s[10]), [s11] "v"(s[11]), [s12] "v"(s[12]),
+          [s13] "v"(s[13]), [s14] "v"(s[14]), [s15] "v"(s[15]));
+#endif
+    return row;
+}
+
 // One workgroup = WAVES waves (4, or 8 at D = 128 and 256 so that one
 // centroid stream per CU feeds two waves per SIMD); wave w owns P blocks of
 // 32 points.  Grid: x = point workgroups, y = K-ranges of k_chunk centroids.
@@ -192,7 +280,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, KM_LDS void *dst
 // Reduction per (tile, point block), per lane (16 scores of one point):
 //   m = min(best, s_0..s_15)           8 v_min3 (NaN inputs are ignored)
 //   if m < best (strict; taken less and less often as K advances):
-//       slot = lowest r with s_r == m  (inline-constant selects)
+//       slot = lowest r with s_r == m  (compare/select pairs, no stalls)
 //       best = m, best_tile = tile, best_slot = slot
 // m is always one of its inputs, so the winner is exact; a strict '<' keeps
 // the earlier tile on equal scores, and the slot search keeps the lower row.
@@ -314,11 +402,6 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                 v[m] = *reinterpret_cast<const f32x4 *>(&stage[r0 + 16 * m + 4 * kq]);
         }
     };
-    // Tile row of element e of A block m, less this lane's 4*kq.
-    auto row_of = [](int m, int e) constexpr {
-        return G == 32 ? 8 * (e >> 2) + (e & 3) : 16 * m + e;
-    };
-
     bf16x8 a[MB][NKS];
     accv ninit[MB];
 
@@ -330,8 +413,9 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         bt[p] = kNoLabel;
         bo[p] = 0;
     }
-    // Fold the scores of point block p in v (centroid kt + row_of(m, e) +
-    // 4*kq) into that block's running best.
+    // Fold the scores of point block p in v (centroid kt + the element's tile
+    // row, as the lowest_row_of_min_* helpers map it, + 4*kq) into that
+    // block's running best.
     auto reduce = [&](int p, const accv (&v)[MB], int kt) KM_INLINE {
         float mn = bs[p];
 #pragma unroll
@@ -340,12 +424,11 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
             for (int r = 0; r < AV; r += 2)
                 mn = __builtin_fminf(__builtin_fminf(mn, v[m][r]), v[m][r + 1]);
         if (mn < bs[p]) {
-            int slot = 0;
-#pragma unroll
-            for (int m = MB - 1; m >= 0; --m)
-#pragma unroll
-                for (int r = AV - 1; r >= 0; --r)
-                    slot = v[m][r] == mn ? row_of(m, r) : slot;
+            int slot;
+            if constexpr (G == 16)
+                slot = lowest_row_of_min_16x16(v[0], v[1], mn);
+            else
+                slot = lowest_row_of_min_32x32(v[0], mn);
             bs[p] = mn;
             bt[p] = kt;
             bo[p] = slot;

@@ -574,7 +574,8 @@ def main():
     if not args.no_ceiling:
         print("[bench] MFMA-only probe on this workload's operands", file=sys.stderr, flush=True)
         X0, C0 = host_sets[0]
-        ceiling = mfma_ceiling(X0, C0, dev, torch.cuda.get_device_properties(dev).multi_processor_count)
+        ceiling = mfma_ceiling(X0, C0, dev, torch.cuda.get_device_properties(dev).multi_processor_count,
+                               settle_ms=args.settle_ms)
         ceiling["assign_frac_of_ceiling"] = round(achieved / ceiling["tflops"], 4)
 
     cpu = None

@@ -164,6 +164,42 @@ def test_workload5_duplicates_and_equal_rows(workload5):
     parity.check(X, C, lab, md, idx=near_dup)
 
 
+# Every pair of rows inside one 32-row tile, and a few triples, made
+# bitwise identical; the points sit next to the copied row, so the copies are
+# each point's nearest centroids with exactly equal scores and the lowest
+# index must win.  Covers the in-lane slot search (which rows a lane holds
+# depends on the MFMA layout: D = 64 and 512 use one, 128 and 256 the other)
+# and the merge across the lanes of a point.
+def _tile_ties(D, seed):
+    rng = np.random.default_rng(seed)
+    groups = [(i, j) for i in range(32) for j in range(i + 1, 32)]
+    groups += [(0, 16, 17), (3, 19, 31), (4, 8, 12), (0, 1, 2), (28, 29, 30)]
+    per = 4                                        # points per tile
+    K = 32 * len(groups)
+    C = rng.standard_normal((K, D), dtype=np.float32)
+    X = np.empty((per * len(groups), D), dtype=np.float32)
+    want = np.empty(per * len(groups), dtype=np.int64)
+    for t, g in enumerate(groups):
+        base = 32 * t
+        for r in g[1:]:
+            C[base + r] = C[base + g[0]]
+        X[per * t:per * (t + 1)] = C[base + g[0]] + 0.01 * rng.standard_normal((per, D), dtype=np.float32)
+        want[per * t:per * (t + 1)] = base + g[0]
+    return W.f32_to_bf16_bits(X), W.f32_to_bf16_bits(C), want
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+def test_ties_inside_a_tile_every_row_pair(D):
+    X, C, want = _tile_ties(D, 1000 + D)
+    ref = oracle.assign(X, C)
+    assert np.array_equal(ref["labels"], want)     # the construction does what it says
+    for path, count in ((km.PATH_AUTO, 0), (km.PATH_SPLIT, 3)):
+        lab, md = run(X, C, path, count)
+        bad = np.flatnonzero(lab != want)
+        assert bad.size == 0, (D, path, [(int(b), int(lab[b]), int(want[b])) for b in bad[:5]])
+        parity.check(X, C, lab, md)
+
+
 def test_nonfinite_centroids():
     X, C, _ = W.gaussian_mixture(700, 64, 300, 77)
     C[3, 5] = W.BF16_QNAN

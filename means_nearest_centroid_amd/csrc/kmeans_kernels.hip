@@ -170,48 +170,95 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, KM_LDS void *dst
 }
 
 // Lowest row, among the rows one lane holds in a tile, whose score equals m
-// (the minimum of those scores).  v_cmp_eq_f32 treats -0 and +0 as equal,
-// as '==' does.  Written as assembly so that compares and selects alternate
-// through three rotating SGPR pairs, each select two instructions behind the
-// compare it reads: the compiler's form sends every compare through VCC and
-// must wait two cycles before each select, a serial chain with a stall per
-// score.  Runs only on lanes whose best improved (under the exec mask of
-// the caller's branch).
+// (the minimum of those scores and of the running best, which m beats).
+// The scores come in pairs, in the order the running minimum took them: t[k]
+// is that minimum after pair k, so the first k with t[k] == m names the
+// first pair holding m (the last pair if none does), and one more compare
+// tells whether it is the pair's first score.  v_cmp_eq_f32 treats -0 and +0
+// as equal, as '==' does; a NaN score never equals m.  Written as assembly:
+// the compares go to separate SGPR pairs, each read two or more
+// instructions after it is written, so no wait states are needed (the
+// compiler's form sends every compare through VCC and waits two cycles
+// before each select).  Runs only on lanes whose best improved (under the
+// exec mask of the caller's branch).
 //
-// 16x16x32 layout: scores a[0..3] are tile rows 0..3 and b[0..3] rows
-// 16..19 (plus the lane's 4 * (lane / 16), added by the caller).
+// 16x16x32 layout: scores a[0..3] are tile rows 0..3, b[0..3] rows 16..19
+// (plus the lane's 4 * (lane / 16), added by the caller); pairs (a0, a1),
+// (a2, a3), (b0, b1), (b2, b3).
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ int lowest_row_of_min_16x16(const f32x4 &a, const f32x4 &b, float m) {
+__device__ __forceinline__ int lowest_row_of_min_16x16(const f32x4 &a, const f32x4 &b,
+                                                       const float (&t)[4], float m) {
     int row = 0;
 #if defined(__HIP_DEVICE_COMPILE__)
-    uint64_t ka, kb, kc;
+    int e, r;
+    uint64_t k1, k2, k3, kd, kc;
     asm volatile(
-        "v_cmp_eq_f32_e64 %[ka], %[b3], %[m]\n\t"
-        "v_cmp_eq_f32_e64 %[kb], %[b2], %[m]\n\t"
-        "v_cmp_eq_f32_e64 %[kc], %[b1], %[m]\n\t"
-        "v_cndmask_b32_e64 %[row], 0, 19, %[ka]\n\t"
-        "v_cmp_eq_f32_e64 %[ka], %[b0], %[m]\n\t"
-        "v_cndmask_b32_e64 %[row], %[row], 18, %[kb]\n\t"
-        "v_cmp_eq_f32_e64 %[kb], %[a3], %[m]\n\t"
-        "v_cndmask_b32_e64 %[row], %[row], 17, %[kc]\n\t"
-        "v_cmp_eq_f32_e64 %[kc], %[a2], %[m]\n\t"
-        "v_cndmask_b32_e64 %[row], %[row], 16, %[ka]\n\t"
-        "v_cmp_eq_f32_e64 %[ka], %[a1], %[m]\n\t"
-        "v_cndmask_b32_e64 %[row], %[row], 3, %[kb]\n\t"
-        "v_cmp_eq_f32_e64 %[kb], %[a0], %[m]\n\t"
-        "v_cndmask_b32_e64 %[row], %[row], 2, %[kc]\n\t"
-        "v_cndmask_b32_e64 %[row], %[row], 1, %[ka]\n\t"
-        "v_cndmask_b32_e64 %[row], %[row], 0, %[kb]"
-        : [row] "=&v"(row), [ka] "=&s"(ka), [kb] "=&s"(kb), [kc] "=&s"(kc)
-        : [m] "v"(m), [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]),
-          [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]));
+        "v_cmp_eq_f32_e64 %[k3], %[t3], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k2], %[t2], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k1], %[t1], %[m]\n\t"
+        "v_cndmask_b32_e64 %[e], %[b2], %[b0], %[k3]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[a2], %[k2]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[a0], %[k1]\n\t"
+        "v_cmp_neq_f32_e64 %[kd], %[e], %[m]\n\t"
+        "v_cndmask_b32_e64 %[r], 18, 16, %[k3]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 2, %[k2]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 0, %[k1]\n\t"
+        "v_addc_co_u32_e64 %[row], %[kc], %[r], 0, %[kd]"
+        : [row] "=&v"(row), [e] "=&v"(e), [r] "=&v"(r), [k1] "=&s"(k1), [k2] "=&s"(k2),
+          [k3] "=&s"(k3), [kd] "=&s"(kd), [kc] "=&s"(kc)
+        : [m] "v"(m), [t1] "v"(t[0]), [t2] "v"(t[1]), [t3] "v"(t[2]), [a0] "v"(a[0]),
+          [a2] "v"(a[2]), [b0] "v"(b[0]), [b2] "v"(b[2]));
 #endif
     return row;
 }
 
 // 32x32x16 layout: score e (0..15) is tile row 8 * (e / 4) + e % 4 (plus the
-// lane's 4 * (lane / 32)).
-__device__ __forceinline__ int lowest_row_of_min_32x32(const f32x16 &s, float m) {
+// lane's 4 * (lane / 32)); pairs (s0, s1), (s2, s3), ..., (s14, s15).
+__device__ __forceinline__ int lowest_row_of_min_32x32(const f32x16 &s, const float (&t)[8],
+                                                       float m) {
+    int row = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    int e, r;
+    uint64_t k1, k2, k3, k4, k5, k6, k7, kd, kc;
+    asm volatile(
+        "v_cmp_eq_f32_e64 %[k7], %[t7], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k6], %[t6], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k5], %[t5], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k4], %[t4], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k3], %[t3], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k2], %[t2], %[m]\n\t"
+        "v_cmp_eq_f32_e64 %[k1], %[t1], %[m]\n\t"
+        "v_cndmask_b32_e64 %[e], %[s14], %[s12], %[k7]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[s10], %[k6]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[s8], %[k5]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[s6], %[k4]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[s4], %[k3]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[s2], %[k2]\n\t"
+        "v_cndmask_b32_e64 %[e], %[e], %[s0], %[k1]\n\t"
+        "v_cmp_neq_f32_e64 %[kd], %[e], %[m]\n\t"
+        "v_cndmask_b32_e64 %[r], 26, 24, %[k7]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 18, %[k6]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 16, %[k5]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 10, %[k4]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 8, %[k3]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 2, %[k2]\n\t"
+        "v_cndmask_b32_e64 %[r], %[r], 0, %[k1]\n\t"
+        "v_addc_co_u32_e64 %[row], %[kc], %[r], 0, %[kd]"
+        : [row] "=&v"(row), [e] "=&v"(e), [r] "=&v"(r), [k1] "=&s"(k1), [k2] "=&s"(k2),
+          [k3] "=&s"(k3), [k4] "=&s"(k4), [k5] "=&s"(k5), [k6] "=&s"(k6), [k7] "=&s"(k7),
+          [kd] "=&s"(kd), [kc] "=&s"(kc)
+        : [m] "v"(m), [t1] "v"(t[0]), [t2] "v"(t[1]), [t3] "v"(t[2]), [t4] "v"(t[3]),
+          [t5] "v"(t[4]), [t6] "v"(t[5]), [t7] "v"(t[6]), [s0] "v"(s[0]), [s2] "v"(s[2]),
+          [s4] "v"(s[4]), [s6] "v"(s[6]), [s8] "v"(s[8]), [s10] "v"(s[10]),
+          [s12] "v"(s[12]), [s14] "v"(s[14]));
+#endif
+    return row;
+}
+
+// The same without the running minima (fewer live registers, where the
+// register budget has no room for them): one compare/select per score,
+// from the last score to the first, through three rotating SGPR pairs.
+__device__ __forceinline__ int lowest_row_of_min_32x32_chain(const f32x16 &s, float m) {
     int row = 0;
 #if defined(__HIP_DEVICE_COMPILE__)
     uint64_t ka, kb, kc;
@@ -417,18 +464,24 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     // row, as the lowest_row_of_min_* helpers map it, + 4*kq) into that
     // block's running best.
     auto reduce = [&](int p, const accv (&v)[MB], int kt) KM_INLINE {
+        // Running minimum over the scores in pairs; t[k] after pair k.
+        float t[MB * AV / 2];
         float mn = bs[p];
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
-            for (int r = 0; r < AV; r += 2)
+            for (int r = 0; r < AV; r += 2) {
                 mn = __builtin_fminf(__builtin_fminf(mn, v[m][r]), v[m][r + 1]);
+                t[(m * AV + r) / 2] = mn;
+            }
         if (mn < bs[p]) {
             int slot;
             if constexpr (G == 16)
-                slot = lowest_row_of_min_16x16(v[0], v[1], mn);
+                slot = lowest_row_of_min_16x16(v[0], v[1], t, mn);
+            else if constexpr (KS < 32)
+                slot = lowest_row_of_min_32x32(v[0], t, mn);
             else
-                slot = lowest_row_of_min_32x32(v[0], mn);
+                slot = lowest_row_of_min_32x32_chain(v[0], mn);
             bs[p] = mn;
             bt[p] = kt;
             bo[p] = slot;

@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kmeans_internal.h"
 
 namespace kmeans {
@@ -82,6 +84,38 @@ __device__ __forceinline__ int swz(int row, int c) {
         return c ^ (row & 15);
     else
         return c ^ ((row / (16 / S)) & (S - 1));
+}
+
+// The values of lane l and lane l ^ OFF (OFF = 16 or 32), in registers:
+// v_permlane16_swap / v_permlane32_swap of a value with its own copy leave
+// the lower lane's value in one result and the upper lane's in the other,
+// in both lanes of the pair (no LDS round trip, unlike ds_bpermute).
+// Callers combine the two symmetrically, so which is which does not matter.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(uint32_t x, uint32_t &u, uint32_t &w) {
+    static_assert(OFF == 16 || OFF == 32, "pairs 16 or 32 lanes apart");
+    if constexpr (OFF == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        u = r[0];
+        w = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        u = r[0];
+        w = r[1];
+    }
+}
+
+// Sum of x over the lanes l, l ^ G, ... that hold one point (G = 16: four
+// lanes, G = 32: two); every one of them gets the same bits.
+template <int G>
+__device__ __forceinline__ float point_lane_sum(float x) {
+    uint32_t u, w;
+    if constexpr (G == 16) {
+        lane_pair<16>(__float_as_uint(x), u, w);
+        x = __uint_as_float(u) + __uint_as_float(w);
+    }
+    lane_pair<32>(__float_as_uint(x), u, w);
+    return __uint_as_float(u) + __uint_as_float(w);
 }
 
 // (s, i) strictly before (so, io) under score-then-index order.
@@ -474,7 +508,9 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                 mn = __builtin_fminf(__builtin_fminf(mn, v[m][r]), v[m][r + 1]);
                 t[(m * AV + r) / 2] = mn;
             }
-        if (mn < bs[p]) {
+        const bool improved = mn < bs[p];
+        bs[p] = mn;                // mn <= bs[p]: the same value when not improved
+        if (improved) {
             int slot;
             if constexpr (G == 16)
                 slot = lowest_row_of_min_16x16(v[0], v[1], t, mn);
@@ -482,7 +518,6 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                 slot = lowest_row_of_min_32x32(v[0], t, mn);
             else
                 slot = lowest_row_of_min_32x32_chain(v[0], mn);
-            bs[p] = mn;
             bt[p] = kt;
             bo[p] = slot;
         }
@@ -573,9 +608,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
             xb[p][ks] = neg2_and_square(xb[p][ks], xx[p]);
-#pragma unroll
-        for (int off = G; off < 64; off <<= 1)
-            xx[p] += __shfl_xor(xx[p], off);
+        xx[p] = point_lane_sum<G>(xx[p]);
     }
 
     wait_vmem();      // block 0, its norms and the points, in one round trip
@@ -630,15 +663,18 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     for (int p = 0; p < PB; ++p) {
         float s = bs[p];
         int32_t i = bt[p] == kNoLabel ? kNoLabel : bt[p] + bo[p] + 4 * kq;
-#pragma unroll
-        for (int off = G; off < 64; off <<= 1) {
-            const float so = __shfl_xor(s, off);
-            const int32_t io = __shfl_xor(i, off);
-            if (pair_before(so, io, s, i)) {
-                s = so;
-                i = io;
-            }
-        }
+        auto merge = [&](auto off) KM_INLINE {
+            uint32_t su, sw, iu, iw;
+            lane_pair<decltype(off)::value>(__float_as_uint(s), su, sw);
+            lane_pair<decltype(off)::value>(static_cast<uint32_t>(i), iu, iw);
+            const bool w_first = pair_before(__uint_as_float(sw), static_cast<int32_t>(iw),
+                                             __uint_as_float(su), static_cast<int32_t>(iu));
+            s = __uint_as_float(w_first ? sw : su);
+            i = static_cast<int32_t>(w_first ? iw : iu);
+        };
+        if constexpr (G == 16)
+            merge(std::integral_constant<int, 16>{});
+        merge(std::integral_constant<int, 32>{});
         const int n = wg_point0 + wave * P * kTileCols + p * G + pcol;
         if (kq == 0 && n < N) {
             if (write_partials) {

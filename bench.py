@@ -300,6 +300,41 @@ def mfma_ceiling(X, C, dev, cus: int, tiles: int = 401, launches: int = 30,
                 zero_operand_tflops=round(zero, 1))
 
 
+def measure_sclk(step, n_steps: int, step_ms: float, dev):
+    """Shader clock while ``step`` runs, untimed: one sleeping wave per XCD
+    (kmeans_clock_sampler, on a side stream of default priority) reads the
+    shader-clock counter against the 100 MHz counter over most of
+    ``n_steps`` back-to-back steps.  The sampler needs a few registers and
+    no LDS, so it sits beside the assign workgroups without displacing
+    them.  Returns the clock per XCD in MHz."""
+    import ctypes
+    import torch
+    from means_nearest_centroid_amd import build as kbuild
+    lib = ctypes.CDLL(kbuild.PROBE_LIBRARY)
+    lib.kmeans_clock_sampler.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p]
+    lib.kmeans_clock_sampler.restype = ctypes.c_int32
+    wgs = 8
+    out = torch.zeros(4 * wgs, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    main = torch.cuda.current_stream()
+    duration_us = max(1, int(0.8 * n_steps * step_ms * 1e3))
+    torch.cuda.synchronize()
+    st = lib.kmeans_clock_sampler(out.data_ptr(), wgs, duration_us, side.cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"kmeans_clock_sampler failed ({st})")
+    for i in range(n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    o = out.view(wgs, 4).cpu().numpy()
+    by_xcd = {}
+    for real, shader, xcd, _ in o:
+        if real > 0:
+            by_xcd.setdefault(int(xcd), []).append(100.0 * float(shader) / float(real))
+    del main
+    return {x: float(np.mean(v)) for x, v in sorted(by_xcd.items())}
+
+
 def cpu_baseline(X, C, target_s: float):
     """Time the oracle on the first points of the workload, growing the
     sample until one run takes about ``target_s`` seconds."""
@@ -570,6 +605,18 @@ def main():
                     avg_launch_us=round(avg_assign_s * 1e6, 2),
                     flop_per_launch=flops)
 
+    sclk = None
+    if not args.no_ceiling:
+        print("[bench] shader clock beside 30 untimed steps", file=sys.stderr, flush=True)
+        by_xcd = measure_sclk(step, 30, ms_per_step, dev)
+        if by_xcd:
+            mhz = float(np.mean(list(by_xcd.values())))
+            sclk = dict(method="one sleeping wave per XCD reads s_memtime against the 100 MHz "
+                               "s_memrealtime beside 30 untimed steps",
+                        mhz_mean=round(mhz, 0),
+                        mhz_by_xcd={str(k): round(v, 0) for k, v in by_xcd.items()},
+                        frac_at_sclk=round(achieved / (BF16_DENSE_PEAK_TFLOPS * mhz / 2400.0), 4))
+
     ceiling = None
     if not args.no_ceiling:
         print("[bench] MFMA-only probe on this workload's operands", file=sys.stderr, flush=True)
@@ -606,6 +653,7 @@ def main():
         },
         "roofline": roofline,
         "mfma_ceiling": ceiling,
+        "sclk": sclk,
         "cpu_baseline": cpu,
         "breakdown_us": {
             "norms_median": round(float(np.median(norms_ms)) * 1e3, 2),

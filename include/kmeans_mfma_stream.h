@@ -44,6 +44,26 @@ int32_t kmeans_mfma_stream(const void *a_rows, const void *b_rows, int32_t rows,
 /* Threads per workgroup of kmeans_mfma_stream. */
 int32_t kmeans_mfma_stream_threads(void);
 
+/*
+ * Shader clock sampler, to run beside another kernel (on another stream) and
+ * read the clock it ran at.  Launches `workgroups` one-wave workgroups; each
+ * sleeps (s_sleep) for `duration_us` microseconds of the constant 100 MHz
+ * counter and writes to out[4w .. 4w+3]: the 100 MHz ticks elapsed, the
+ * shader-clock ticks elapsed over the same interval (clock in MHz = 100 *
+ * out[4w+1] / out[4w]), the XCD id it ran on, 0.  With the default
+ * round-robin dispatch, workgroup w runs on XCD w % 8.  Asynchronous on
+ * `stream`.
+ *
+ *   out          uint64 [4 * workgroups], device, 8-byte aligned, written
+ *   workgroups   1..1024
+ *   duration_us  1..10^7
+ *
+ * Returns 0, 1 for an invalid argument (nothing launched), 2 if the launch
+ * failed.
+ */
+int32_t kmeans_clock_sampler(uint64_t *out, int32_t workgroups, int32_t duration_us,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -110,3 +110,45 @@ extern "C" int32_t kmeans_mfma_stream(const void *a_rows, const void *b_rows, in
 }
 
 extern "C" int32_t kmeans_mfma_stream_threads(void) { return kThreads; }
+
+// Shader clock sampler (measurement only).  Each workgroup is one wave that
+// records the shader-clock counter (s_memtime) and the constant 100 MHz
+// counter (s_memrealtime) at its start and again once `ticks` 100 MHz ticks
+// have passed, sleeping in between (s_sleep: it takes almost no issue slots
+// from kernels that share its SIMD).  Run beside another kernel, it gives the
+// clock that kernel ran at; workgroup w lands on XCD w % 8 under the default
+// round-robin dispatch, and its XCD id is recorded too.
+namespace {
+
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64)))
+void clock_sampler_kernel(uint64_t *__restrict__ out, uint64_t ticks) {
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    uint64_t r = r0;
+    // Bounded: at most ~2^20 sleeps of ~8k cycles whatever the counters do.
+    for (int i = 0; i < (1 << 20) && r - r0 < ticks; ++i) {
+        __builtin_amdgcn_s_sleep(127);
+        r = __builtin_amdgcn_s_memrealtime();
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    if (threadIdx.x == 0) {
+        uint64_t *o = out + static_cast<size_t>(blockIdx.x) * 4;
+        o[0] = r - r0;
+        o[1] = c1 - c0;
+        o[2] = static_cast<uint64_t>(__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)));
+        o[3] = 0;
+    }
+}
+
+}  // namespace
+
+extern "C" int32_t kmeans_clock_sampler(uint64_t *out, int32_t workgroups, int32_t duration_us,
+                                        hipStream_t stream) {
+    if (!out || workgroups < 1 || workgroups > 1024 || duration_us < 1 || duration_us > 10000000)
+        return 1;
+    if (reinterpret_cast<uintptr_t>(out) % 8 != 0)
+        return 1;
+    hipLaunchKernelGGL(clock_sampler_kernel, dim3(workgroups), dim3(64), 0, stream, out,
+                       static_cast<uint64_t>(duration_us) * 100u);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}

@@ -46,7 +46,7 @@ def test_probe_library_exports_its_header():
     header = os.path.join(os.path.dirname(km.HEADER), "kmeans_mfma_stream.h")
     text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(kmeans_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["kmeans_mfma_stream", "kmeans_mfma_stream_threads"]
+    assert names == ["kmeans_clock_sampler", "kmeans_mfma_stream", "kmeans_mfma_stream_threads"]
     for name in names:
         assert hasattr(probe, name)
     assert probe.kmeans_mfma_stream_threads() == 256
@@ -57,6 +57,13 @@ def test_probe_library_exports_its_header():
     assert f(FAKE, FAKE, 0, 10, 1, FAKE, NUL) == 1
     assert f(FAKE, FAKE, 64, 10, 70000, FAKE, NUL) == 1
     assert f(FAKE_ODD, FAKE, 64, 10, 1, FAKE, NUL) == 1
+    g = probe.kmeans_clock_sampler
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert g(None, 8, 100, NUL) == 1
+    assert g(FAKE, 0, 100, NUL) == 1
+    assert g(FAKE, 2000, 100, NUL) == 1
+    assert g(FAKE, 8, 0, NUL) == 1
+    assert g(FAKE_ODD, 8, 100, NUL) == 1
 
 
 def test_abi_version(lib):

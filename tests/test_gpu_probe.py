@@ -65,3 +65,21 @@ def test_probe_rejects_bad_arguments(probe):
     assert st == 1
     st, _ = run(probe, z, z, 64, 0, 1)
     assert st == 1
+
+
+def test_clock_sampler_reads_a_plausible_clock(probe):
+    lib = ctypes.CDLL(kbuild.PROBE_LIBRARY)
+    lib.kmeans_clock_sampler.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p]
+    lib.kmeans_clock_sampler.restype = ctypes.c_int32
+    out = torch.zeros(4 * 8, dtype=torch.int64, device="cuda")
+    st = lib.kmeans_clock_sampler(out.data_ptr(), 8, 2000,
+                                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    o = out.view(8, 4).cpu().numpy()
+    assert np.all(o[:, 0] >= 2000 * 100)            # at least the requested 100 MHz ticks
+    assert np.all(o[:, 0] < 2000 * 100 * 10)        # and the loop ended
+    mhz = 100.0 * o[:, 1] / o[:, 0]
+    assert np.all((mhz > 100) & (mhz < 4000)), mhz
+    assert np.all(o[:, 3] == 0)

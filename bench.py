@@ -40,8 +40,11 @@ BF16_DENSE_PEAK_TFLOPS = 2516.6     # MI355X: 256 CU x 4096 flop/clk x 2.4 GHz
 KERNEL_SOURCES = ("means_nearest_centroid_amd/csrc/kmeans_kernels.hip",
                   "means_nearest_centroid_amd/csrc/kmeans_internal.h",
                   "means_nearest_centroid_amd/csrc/kmeans_api.hip")
-UPDATE_SOURCES = KERNEL_SOURCES + ("means_nearest_centroid_amd/csrc/kmeans_update.hip",
-                                   "means_nearest_centroid_amd/csrc/kmeans_update_internal.h")
+# The update's kernels are built from these alone (kmeans_kernels.hip and
+# the host-side kmeans_api.hip play no part in them).
+UPDATE_SOURCES = ("means_nearest_centroid_amd/csrc/kmeans_update.hip",
+                  "means_nearest_centroid_amd/csrc/kmeans_update_internal.h",
+                  "means_nearest_centroid_amd/csrc/kmeans_internal.h")
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 
 

@@ -817,15 +817,17 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
 
     // Too few wide point tiles to fill the GPU: first try narrow tiles (one
     // point block per wave) if they fit in one round and K is at most 16
-    // centroid blocks; otherwise split K, aiming at about 3/4 of the
-    // workgroups the GPU holds at once, with at least two centroid blocks per
-    // K-range (the merge pass and the extra launch cost ~10 us, which a
-    // one-block range does not earn back).  Measured at N = 65536 (median
-    // us): D=64 K=4096: wide split 3 54, narrow 45; D=64 K=512: wide 19,
-    // narrow 11; D=64 K=16384: split 3 149, narrow 146; D=128 K=512: wide 21,
-    // narrow 16; D=128 K=4096: split 2 68, narrow 70; D=128 K=16384: split 2
-    // 216, narrow 235, split 3 271; N=4096 D=64 K=256: wide 13, narrow 7.
-    const int target_wgs = 3 * resident / 4;
+    // centroid blocks; otherwise split K into enough ranges for one full
+    // round of workgroups, with at least two centroid blocks per K-range
+    // (every range pays the point prologue and the merge pass costs a
+    // launch, which a one-block range does not earn back).  Measured at
+    // N = 65536 (median us, settled): D=64 K=16384: split 2 125.5, 3 131.4,
+    // 4 (one round) 119.2, 6 127.0, narrow 131.1; D=64 K=4096: narrow 36.7,
+    // split 3 42.3, 4 43.5; D=64 K=512: narrow 8.9, wide 13.9, split ~30;
+    // D=128 K=4096: narrow 56.9, split 2 58.1, wide 89.2; D=128 K=512:
+    // narrow 12.0, wide 18.7; D=256 K=4096: wide 104.8, narrow 106.3, split 2
+    // 117.1.  N=262144 D=128 K=16384: wide direct 724.8, split 2 749.4.
+    const int target_wgs = resident;
     int pb = wide;
     if (force_path == 1 && force_count == 1)
         pb = 1;

@@ -152,7 +152,7 @@ def test_plan_for_the_workloads(lib):
 # is at most 16 centroid blocks, the K-split above that, wide tiles at large N.
 SWEEP_PLANS = {
     (65536, 64, 512): (1, 1, 128), (65536, 64, 4096): (1, 1, 128),
-    (65536, 64, 16384): (2, 3, 512), (65536, 128, 512): (1, 1, 256),
+    (65536, 64, 16384): (2, 4, 512), (65536, 128, 512): (1, 1, 256),
     (65536, 128, 4096): (1, 1, 256), (262144, 128, 4096): (1, 1, 512),
     (262144, 128, 16384): (1, 1, 512), (1048576, 128, 4096): (1, 1, 512),
     (65536, 256, 512): (1, 1, 256), (65536, 256, 4096): (1, 1, 256),
@@ -173,7 +173,7 @@ def test_plan_for_the_sweep_shapes(lib):
 def test_plan_follows_the_compute_unit_count(lib):
     assert km.kmeans_plan(65536, 128, 16384, 256)["splits"] == 2
     assert km.kmeans_plan(65536, 128, 16384, 128)["path"] == km.PATH_DIRECT
-    assert km.kmeans_plan(65536, 128, 16384, 1024)["splits"] == 6
+    assert km.kmeans_plan(65536, 128, 16384, 1024)["splits"] == 8   # one full round
     # narrow tiles only when they fit in one round
     assert km.kmeans_plan(65536, 64, 4096, 256)["points_per_wg"] == 128
     assert km.kmeans_plan(65536, 64, 4096, 64)["points_per_wg"] == 512

@@ -14,8 +14,9 @@
 // the data, so a call gives the same bits every time.
 //
 //  1. Points are grouped by label with a stable LSD radix sort of the keys
-//     (label, or K for a stray label) carrying the point index, on 8-bit
-//     digits.  A pass is: a per-tile digit histogram, one exclusive scan over
+//     (label, or K for a stray label) carrying the point index, on digits
+//     of at most 8 bits, the key's bits split evenly over the passes (7 + 6
+//     at K = 4096).  A pass is: a per-tile digit histogram, one exclusive scan over
 //     (digit, tile) -- done by every scatter workgroup for its own tile when
 //     there are at most 128 tiles, by a scan kernel beyond -- and a scatter
 //     in which every tile ranks its keys in index order: wave ballots give
@@ -78,13 +79,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 // ---- 1. radix sort -------------------------------------------------------
 
-// Digit histogram of one tile for the pass on (key >> shift) & 255, written
-// digit-major ([digit][tile]).  FIRST: keys come from the labels, and the
-// launch also clears the cluster bounds (clear, n_clear entries).
+// Digit histogram of one tile for the pass on (key >> shift) & mask, written
+// digit-major ([digit][tile], all 256 rows; rows above mask count zero).
+// FIRST: keys come from the labels, and the launch also clears the cluster
+// bounds (clear, n_clear entries).
 template <bool FIRST>
 __global__ __launch_bounds__(kSortThreads)
-void upd_hist_kernel(const int32_t *__restrict__ keys_in, int N, int K, int shift, int tile_log2,
-                     int tiles, int stride, int32_t *__restrict__ hist, int32_t *__restrict__ clear,
+void upd_hist_kernel(const int32_t *__restrict__ keys_in, int N, int K, int shift, int mask,
+                     int tile_log2, int tiles, int stride, int32_t *__restrict__ hist, int32_t *__restrict__ clear,
                      int64_t n_clear) {
     __shared__ int h[kRadix];
     const int tid = threadIdx.x;
@@ -96,7 +98,7 @@ void upd_hist_kernel(const int32_t *__restrict__ keys_in, int N, int K, int shif
                                          static_cast<int64_t>(beg) + (int64_t(1) << tile_log2)));
     for (int i = beg + tid; i < fin; i += kSortThreads) {
         const int key = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
-        atomicAdd(&h[(key >> shift) & (kRadix - 1)], 1);
+        atomicAdd(&h[(key >> shift) & mask], 1);
     }
     __syncthreads();
     int32_t *row = hist + static_cast<size_t>(tid) * stride;
@@ -190,7 +192,7 @@ void upd_scan_kernel(int32_t *__restrict__ h, int M) {
     }
 }
 
-// One stable scatter pass on digit (key >> shift) & 255.  hist is this
+// One stable scatter pass on digit (key >> shift) & mask.  hist is this
 // pass's histogram ([digit][stride]); SCANNED: it holds exclusive offsets
 // already (the scan kernel ran), else each workgroup derives its own 256
 // offsets from the raw counts (four threads sum each digit's row, the
@@ -198,15 +200,15 @@ void upd_scan_kernel(int32_t *__restrict__ h, int M) {
 // from the labels and the values are the point indices.
 //
 // A round places 1024 keys (16 waves): each wave finds the lanes sharing
-// its digit with 8 ballots (rank = earlier such lanes) and the group's last
+// its digit with one ballot per digit bit (rank = earlier such lanes) and the group's last
 // lane records the count, tagged with the round, in wcnt[wave][digit]; the
 // owner thread of each digit then turns the 16 counts into per-wave starts
 // (its running position plus the counts of earlier waves).
 template <bool FIRST, bool SCANNED>
 __global__ __launch_bounds__(kScatterThreads)
 void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__restrict__ vals_in,
-                        int N, int K, int shift, int tile_log2, int tiles, int stride,
-                        const int32_t *__restrict__ hist, int32_t *__restrict__ keys_out,
+                        int N, int K, int shift, int mask, int tile_log2, int tiles,
+                        int stride, const int32_t *__restrict__ hist, int32_t *__restrict__ keys_out,
                         int32_t *__restrict__ vals_out) {
     typedef int32_t i4 __attribute__((ext_vector_type(4)));
     constexpr int kWaves = kScatterThreads / 64;
@@ -248,16 +250,20 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
             run = hist[static_cast<size_t>(tid) * stride + t];
     } else {
         // Digit d's counts in earlier tiles and in all tiles (stride <= 128):
-        // four threads per digit each sum a quarter of its row.
+        // four threads per digit each sum a quarter of its row.  Digits above
+        // the mask, and above K >> shift (keys are at most K), never occur:
+        // their rows hold zeros and are not read (at K = 4096, 128 of the
+        // 256 rows in the first pass and 223 in the second).
         const int d = tid & (kRadix - 1);
         const int qq = tid >> 8;
+        const bool live = d <= min(mask, K >> shift);
         constexpr int kG = kFusedScanTiles / 16;        // 16-byte groups per quarter
         const i4 *rv = reinterpret_cast<const i4 *>(hist + static_cast<size_t>(d) * stride) +
                        qq * kG;
         i4 v[kG];
 #pragma unroll
         for (int g = 0; g < kG; ++g)
-            v[g] = (qq * kG + g) * 4 < stride ? rv[g] : i4{0, 0, 0, 0};
+            v[g] = live && (qq * kG + g) * 4 < stride ? rv[g] : i4{0, 0, 0, 0};
         int pre = 0, tot = 0;
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
@@ -308,10 +314,12 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
             ++tag;
             const bool valid = base + tid < len;
             const int key = bkey[r];
-            const int d = (key >> shift) & (kRadix - 1);
+            const int d = (key >> shift) & mask;
             uint64_t same = __ballot(valid);
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
+                if ((mask >> b) == 0)
+                    break;                     // uniform: no digit bit b
                 const bool bit = (d >> b) & 1;
                 const uint64_t m = __ballot(valid && bit);
                 same &= bit ? m : ~m;
@@ -718,6 +726,9 @@ UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units) 
     while ((int64_t(1) << bits) <= K)
         ++bits;                                   // keys run 0..K
     p.passes = (bits + 7) / 8;
+    // Even digits (K = 4096: 7 + 6 bits, not 8 + 5) halve the histogram rows
+    // the first pass's scatter reads and cost the second pass little.
+    p.digit_bits = (bits + p.passes - 1) / p.passes;
     // Sort tiles of 2^tl >= 1024 points: at most 128 tiles while tiles stay
     // <= 16384 points (the scan then holds its histogram in registers), at
     // most 4096 beyond.
@@ -769,7 +780,9 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
         const bool scan = pl.tiles > kFusedScanTiles;
         const dim3 grid(pl.tiles), block(kSortThreads);
         hipError_t e = hipSuccess;
+        const int mask = (1 << pl.digit_bits) - 1;
         for (int q = 0; q < pl.passes && e == hipSuccess; ++q) {
+            const int sh = pl.digit_bits * q;
             int32_t *h = hist + hsz * q;
             const int32_t *kin = q == 0 ? labels : reinterpret_cast<int32_t *>(base + pl.keys[(q - 1) & 1]);
             const int32_t *vin = q == 0 ? nullptr : reinterpret_cast<int32_t *>(base + pl.vals[(q - 1) & 1]);
@@ -777,28 +790,27 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
             vals = reinterpret_cast<int32_t *>(base + pl.vals[q & 1]);
             if (q == 0)   // also clears start and end (adjacent in the workspace)
                 hipLaunchKernelGGL(upd_hist_kernel<true>, grid, block, 0, stream, kin, N, K, 0,
-                                   pl.tile_log2, pl.tiles, pl.stride, h, start,
+                                   mask, pl.tile_log2, pl.tiles, pl.stride, h, start,
                                    static_cast<int64_t>((pl.partial - pl.start) / 4));
             else
-                hipLaunchKernelGGL(upd_hist_kernel<false>, grid, block, 0, stream, kin, N, K, 8 * q,
-                                   pl.tile_log2, pl.tiles, pl.stride, h, nullptr, int64_t(0));
+                hipLaunchKernelGGL(upd_hist_kernel<false>, grid, block, 0, stream, kin, N, K, sh,
+                                   mask, pl.tile_log2, pl.tiles, pl.stride, h, nullptr, int64_t(0));
             if (scan)
                 hipLaunchKernelGGL(upd_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, h,
                                    static_cast<int>(hsz));
-            const int sh = 8 * q;
             const dim3 sblock(kScatterThreads);
             if (q == 0 && scan)
                 hipLaunchKernelGGL((upd_scatter_kernel<true, true>), grid, sblock, 0, stream, kin,
-                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
+                                   vin, N, K, sh, mask, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
             else if (q == 0)
                 hipLaunchKernelGGL((upd_scatter_kernel<true, false>), grid, sblock, 0, stream, kin,
-                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
+                                   vin, N, K, sh, mask, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
             else if (scan)
                 hipLaunchKernelGGL((upd_scatter_kernel<false, true>), grid, sblock, 0, stream, kin,
-                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
+                                   vin, N, K, sh, mask, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
             else
                 hipLaunchKernelGGL((upd_scatter_kernel<false, false>), grid, sblock, 0, stream, kin,
-                                   vin, N, K, sh, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
+                                   vin, N, K, sh, mask, pl.tile_log2, pl.tiles, pl.stride, h, keys, vals);
             e = hipGetLastError();
         }
         if (e != hipSuccess)

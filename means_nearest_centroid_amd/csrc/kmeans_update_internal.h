@@ -8,7 +8,8 @@ namespace kmeans {
 
 // Workspace layout and launch shape of one kmeans_update call.
 struct UpdatePlan {
-    int passes;        // 8-bit radix passes over the keys 0..K (K = stray label)
+    int passes;        // radix passes over the keys 0..K (K = stray label)
+    int digit_bits;    // bits per pass (<= 8): the key bits split evenly
     int tile_log2;     // sort tile of 2^tile_log2 points (>= 1024)
     int tiles;         // sort tiles
     int stride;        // histogram row length: tiles rounded up to 4

@@ -548,14 +548,12 @@ def main():
     def step(i, ev=None):
         X, C = sets[i % len(sets)]
         n = norms[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
         km.kmeans_centroid_norms(C, n, stream=stream)
         if ev is not None:
-            ev[1].record(stream)
+            ev[0].record(stream)
         km.kmeans_assign(X, C, n, labels, min_dist, stream=stream)
         if ev is not None:
-            ev[2].record(stream)
+            ev[1].record(stream)
 
     settled = settle(step, args.settle_ms)
     print(f"[bench] settled clocks with {settled} untimed steps; warmup {args.warmup} steps",
@@ -565,8 +563,11 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K steps bracketed by synchronisation, GPU events on the
-    # launch stream around the whole region and around each kernel.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # launch stream around the whole region and around each assign launch;
+    # a step's norms launch runs alone between the previous step's last
+    # event (or the start) and its own first one, so two events per step
+    # time both kernels.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -579,8 +580,9 @@ def main():
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    norms_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    assign_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    norms_ms = np.array([(start if i == 0 else evs[i - 1][1]).elapsed_time(evs[i][0])
+                         for i in range(args.steps)])
+    assign_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     print(f"[bench] {args.steps} steps: {total_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall",
           file=sys.stderr, flush=True)
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define KMEANS_ABI_VERSION 3
+#define KMEANS_ABI_VERSION 4
 
 /* Supported feature dimension: 16 <= D <= 512 and D % 16 == 0. */
 #define KMEANS_MIN_D 16
@@ -57,7 +57,7 @@ typedef enum {
     KMEANS_ERR_UNSUPPORTED = 2,  /* D outside the supported set; N or K >= 2^31 */
     KMEANS_ERR_ALIGNMENT = 3,    /* X/C not 16-byte or outputs not 4-byte aligned */
     KMEANS_ERR_HIP = 4,          /* a HIP runtime call or launch failed */
-    KMEANS_ERR_NO_MEMORY = 5     /* stream-ordered workspace allocation failed */
+    KMEANS_ERR_NO_MEMORY = 5     /* the stream's workspace could not be allocated */
 } kmeans_status_t;
 
 typedef enum {
@@ -99,10 +99,10 @@ kmeans_status_t kmeans_centroid_norms(const void *C, int64_t K, int64_t D,
  *   min_dist  fp32 [N], written: squared distance to the chosen centroid,
  *             max(0, ||x||^2 + s_best) for finite data.
  *
- * Small-N / large-K shapes run a K-split path whose stream-ordered scratch
- * (8 bytes per point per split + 4 bytes per point) comes from
- * hipMallocAsync/hipFreeAsync on `stream`; KMEANS_ERR_NO_MEMORY if it fails.
- * All paths give bitwise-identical outputs.
+ * Small-N / large-K shapes run a K-split path whose scratch (8 bytes per
+ * point per split + 4 bytes per point) is the stream's workspace (see
+ * kmeans_release_workspace); KMEANS_ERR_NO_MEMORY if it cannot grow.  All
+ * paths give bitwise-identical outputs.
  */
 kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms,
                               int64_t N, int64_t D, int64_t K, int32_t *labels,
@@ -176,13 +176,30 @@ kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_uni
  * label in index order, in chunks of 128 sorted positions whose partial sums
  * add in chunk order), so the outputs are bitwise deterministic; IEEE
  * arithmetic throughout (a NaN coordinate makes that coordinate of the mean
- * NaN).  Scratch of about 16 bytes per point plus 8 bytes per cluster comes
- * from hipMallocAsync/hipFreeAsync on `stream`; KMEANS_ERR_NO_MEMORY if it
- * fails.
+ * NaN).  Scratch of about 16 bytes per point plus 8 bytes per cluster is
+ * the stream's workspace (see kmeans_release_workspace); KMEANS_ERR_NO_MEMORY
+ * if it cannot grow.
  */
 kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
                               int64_t N, int64_t D, int64_t K, void *C_new, float *norms,
                               int32_t *counts, float *means, hipStream_t stream);
+
+/*
+ * The workspace of `stream` on the current device.  kmeans_assign's K-split
+ * path and kmeans_update take their scratch from one device buffer per
+ * (device, stream), kept between calls: a stream-ordered allocation and free
+ * on every call costs more host time than a small call's kernels.  It grows
+ * in stream order (the old buffer freed by hipFreeAsync and a larger one
+ * taken from hipMallocAsync, both on `stream`), so calls on one stream share
+ * it safely and calls on different streams never do.  The library never
+ * frees it by itself: this call returns it to the device's default memory
+ * pool, in stream order, behind the calls already queued on `stream`.  Call
+ * it before destroying a stream that was passed to those entry points (a new
+ * stream could otherwise inherit the buffer while the old stream's calls
+ * still run), or to give the memory back.  No-op when the stream holds
+ * none; KMEANS_ERR_HIP if the free fails.
+ */
+kmeans_status_t kmeans_release_workspace(hipStream_t stream);
 
 /* Thread-local message for the last non-OK status ("" if none). */
 const char *kmeans_last_error(void);

@@ -76,6 +76,8 @@ def load_library(path: str = LIBRARY):
     lib.kmeans_plan.restype = ctypes.c_int
     lib.kmeans_update.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.kmeans_update.restype = ctypes.c_int
+    lib.kmeans_release_workspace.argtypes = [vp]
+    lib.kmeans_release_workspace.restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
     lib.kmeans_last_error.restype = ctypes.c_char_p
     lib.kmeans_abi_version.argtypes = []
@@ -216,6 +218,14 @@ def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=N
                                   _ptr(norms), _ptr(counts), _ptr(means),
                                   _stream_handle(stream)))
     return C_new, norms, counts, means
+
+
+def kmeans_release_workspace(stream=None):
+    """Return the stream's workspace (the K-split path's and the update's
+    scratch, kept between calls) to the device's memory pool, in stream
+    order; a later call on the stream allocates it again."""
+    lib = load_library()
+    _check(lib, lib.kmeans_release_workspace(_stream_handle(stream)))
 
 
 def assign(X, C, norms=None):

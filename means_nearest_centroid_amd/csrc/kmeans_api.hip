@@ -4,7 +4,10 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "kmeans_internal.h"
 #include "kmeans_mi355x.h"
@@ -46,6 +49,58 @@ int device_compute_units() {
         cache[dev].store(cus, std::memory_order_relaxed);
     }
     return cus;
+}
+
+namespace {
+// (device, stream) -> (buffer, bytes).  Never destroyed: at process exit the
+// runtime may be gone before static destructors run, and it reclaims device
+// memory itself.
+std::mutex g_ws_mutex;
+auto *g_ws = new std::map<std::pair<int, uintptr_t>, std::pair<void *, size_t>>();
+constexpr size_t kWorkspaceGranule = size_t(1) << 20;
+}  // namespace
+
+WorkspaceLease::WorkspaceLease(hipStream_t stream, size_t bytes) {
+    g_ws_mutex.lock();
+    int dev = 0;
+    error_ = hipGetDevice(&dev);
+    if (error_ != hipSuccess)
+        return;
+    auto &slot = (*g_ws)[{dev, reinterpret_cast<uintptr_t>(stream)}];
+    if (slot.second < bytes) {
+        if (slot.first != nullptr) {
+            void *old = slot.first;
+            slot = {nullptr, 0};
+            error_ = hipFreeAsync(old, stream);
+            if (error_ != hipSuccess)
+                return;
+        }
+        const size_t want = (bytes + kWorkspaceGranule - 1) / kWorkspaceGranule * kWorkspaceGranule;
+        void *p = nullptr;
+        error_ = hipMallocAsync(&p, want, stream);
+        if (error_ == hipSuccess && p == nullptr)
+            error_ = hipErrorOutOfMemory;
+        if (error_ != hipSuccess)
+            return;
+        slot = {p, want};
+    }
+    ptr_ = slot.first;
+}
+
+WorkspaceLease::~WorkspaceLease() { g_ws_mutex.unlock(); }
+
+hipError_t release_workspace(hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    auto it = g_ws->find({dev, reinterpret_cast<uintptr_t>(stream)});
+    if (it == g_ws->end())
+        return hipSuccess;
+    void *p = it->second.first;
+    g_ws->erase(it);
+    return p != nullptr ? hipFreeAsync(p, stream) : hipSuccess;
 }
 
 kmeans_status_t check_d(int64_t D) {
@@ -134,27 +189,23 @@ kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int
         return ok();
     }
 
-    // Split path: stream-ordered scratch for the partial winners and ||x||^2.
+    // Split path: the stream's scratch holds the partial winners and ||x||^2.
     const size_t per = static_cast<size_t>(N);
     const size_t bytes = per * pl.splits * (sizeof(float) + sizeof(int32_t)) + per * sizeof(float);
-    void *ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, bytes, stream);
-    if (e != hipSuccess || ws == nullptr)
-        return fail(KMEANS_ERR_NO_MEMORY, "hipMallocAsync(%zu) failed: %s", bytes,
-                    hipGetErrorString(e));
-    auto *ws_score = static_cast<float *>(ws);
+    const kmeans::WorkspaceLease lease(stream, bytes);
+    if (lease.error() != hipSuccess)
+        return fail(KMEANS_ERR_NO_MEMORY, "workspace of %zu bytes: %s", bytes,
+                    hipGetErrorString(lease.error()));
+    auto *ws_score = static_cast<float *>(lease.ptr());
     auto *ws_label = reinterpret_cast<int32_t *>(ws_score + per * pl.splits);
     auto *ws_xx = reinterpret_cast<float *>(ws_label + per * pl.splits);
-    e = kmeans::launch_assign(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score, ws_label,
-                              ws_xx, stream);
+    hipError_t e = kmeans::launch_assign(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score,
+                                         ws_label, ws_xx, stream);
     if (e == hipSuccess)
         e = kmeans::launch_merge(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score,
                                  ws_label, ws_xx, stream);
-    hipError_t ef = hipFreeAsync(ws, stream);
     if (e != hipSuccess)
         return fail(KMEANS_ERR_HIP, "split-path launch failed: %s", hipGetErrorString(e));
-    if (ef != hipSuccess)
-        return fail(KMEANS_ERR_HIP, "hipFreeAsync failed: %s", hipGetErrorString(ef));
     return ok();
 }
 
@@ -220,6 +271,13 @@ kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_uni
         *k_block = pl.bk;
     if (padded_d)
         *padded_d = pl.ks * 16;
+    return ok();
+}
+
+kmeans_status_t kmeans_release_workspace(hipStream_t stream) {
+    const hipError_t e = kmeans::release_workspace(stream);
+    if (e != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "releasing the workspace failed: %s", hipGetErrorString(e));
     return ok();
 }
 

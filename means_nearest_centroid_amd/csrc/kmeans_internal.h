@@ -142,4 +142,30 @@ kmeans_status_t check_d(int64_t D);
 // Compute units of the current device (cached per device), or 256.
 int device_compute_units();
 
+// Scratch for one call on `stream`: a buffer of at least `bytes`, kept per
+// (device, stream) between calls, since a hipMallocAsync/hipFreeAsync pair
+// per call costs ~15 us of host time (more than a small call's kernels).  It
+// grows stream-ordered: the old buffer is freed by hipFreeAsync and the new
+// one taken from hipMallocAsync, both on `stream`, behind the work already
+// queued there.  Calls on one stream run in order, so they can share it;
+// another stream gets its own.  The lease holds a process-wide lock until it
+// is destroyed, so no other thread can grow the buffer between this call's
+// acquisition and its launches.
+class WorkspaceLease {
+public:
+    WorkspaceLease(hipStream_t stream, size_t bytes);
+    ~WorkspaceLease();
+    WorkspaceLease(const WorkspaceLease &) = delete;
+    WorkspaceLease &operator=(const WorkspaceLease &) = delete;
+    void *ptr() const { return ptr_; }
+    hipError_t error() const { return error_; }
+
+private:
+    void *ptr_ = nullptr;
+    hipError_t error_ = hipSuccess;
+};
+
+// Frees (stream-ordered) the current device's buffer kept for `stream`.
+hipError_t release_workspace(hipStream_t stream);
+
 }  // namespace kmeans

@@ -821,12 +821,13 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
     // round of workgroups, with at least two centroid blocks per K-range
     // (every range pays the point prologue and the merge pass costs a
     // launch, which a one-block range does not earn back).  Measured at
-    // N = 65536 (median us, settled): D=64 K=16384: split 2 125.5, 3 131.4,
-    // 4 (one round) 119.2, 6 127.0, narrow 131.1; D=64 K=4096: narrow 36.7,
-    // split 3 42.3, 4 43.5; D=64 K=512: narrow 8.9, wide 13.9, split ~30;
-    // D=128 K=4096: narrow 56.9, split 2 58.1, wide 89.2; D=128 K=512:
-    // narrow 12.0, wide 18.7; D=256 K=4096: wide 104.8, narrow 106.3, split 2
-    // 117.1.  N=262144 D=128 K=16384: wide direct 724.8, split 2 749.4.
+    // N = 65536 (median us, settled, scratch kept per stream): D=64 K=16384:
+    // split 2 122.4, 3 127.7, 4 (one round) 113.3, 6 121.7, narrow 129.6;
+    // D=64 K=4096: narrow 36.0, split 3 39.1, 4 37.6; D=64 K=512: narrow
+    // 8.8, wide 13.9, split 12.6; D=128 K=4096: narrow 56.0, split 2 55.2,
+    // wide 89.4; D=128 K=512: narrow 11.4, wide 18.8, split 16.0; D=256
+    // K=4096: wide 104.5, narrow 103.9, split 2 112.7.  N=262144 D=128
+    // K=16384: wide direct 708.0, split 2 730.5.
     const int target_wgs = resident;
     int pb = wide;
     if (force_path == 1 && force_count == 1)

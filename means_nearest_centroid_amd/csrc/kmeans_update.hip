@@ -39,6 +39,8 @@
 //     pre-pass computes it (row_sq_norm16 over a copy of the row in LDS).
 #include <stdint.h>
 
+#include <memory>
+
 #include "kmeans_update_internal.h"
 
 namespace kmeans {
@@ -859,22 +861,22 @@ extern "C" kmeans_status_t kmeans_update(const void *X, const int32_t *labels, c
         return fail(KMEANS_ERR_ALIGNMENT, "labels, norms, counts and means must be 4-byte aligned");
 
     const UpdatePlan pl = make_update_plan(N, D, K, device_compute_units());
+    // The stream's scratch (none when N == 0), held until the launches are queued.
+    std::unique_ptr<WorkspaceLease> lease;
     void *ws = nullptr;
     if (pl.bytes > 0) {
-        hipError_t e = hipMallocAsync(&ws, pl.bytes, stream);
-        if (e != hipSuccess || ws == nullptr)
-            return fail(KMEANS_ERR_NO_MEMORY, "hipMallocAsync(%zu) failed: %s", pl.bytes,
-                        hipGetErrorString(e));
+        lease = std::make_unique<WorkspaceLease>(stream, pl.bytes);
+        if (lease->error() != hipSuccess)
+            return fail(KMEANS_ERR_NO_MEMORY, "workspace of %zu bytes: %s", pl.bytes,
+                        hipGetErrorString(lease->error()));
+        ws = lease->ptr();
     }
     hipError_t e = launch_update(pl, static_cast<const uint16_t *>(X), labels,
                                          static_cast<const uint16_t *>(C_old),
                                          static_cast<int>(N), static_cast<int>(D),
                                          static_cast<int>(K), static_cast<uint16_t *>(C_new),
                                          norms, counts, means, ws, stream);
-    hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
     if (e != hipSuccess)
         return fail(KMEANS_ERR_HIP, "update launch failed: %s", hipGetErrorString(e));
-    if (ef != hipSuccess)
-        return fail(KMEANS_ERR_HIP, "hipFreeAsync failed: %s", hipGetErrorString(ef));
     return ok();
 }

@@ -396,27 +396,33 @@ def run_update(args):
 
     def step(i, ev=None):
         X, lab, C = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
         km.kmeans_update(X, lab, C, C_new, norms, counts, stream=stream)
         if ev is not None:
-            ev[1].record(stream)
+            ev.record(stream)
 
     settled = settle(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # One event after each call: calls run back to back, so call i's time
+    # is the span from the previous call's event (or the start) to its own.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         step(i, evs[i])
     end.record(stream)
+    enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-    call_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    call_ms = np.array([(start if i == 0 else evs[i - 1]).elapsed_time(evs[i])
+                        for i in range(args.steps)])
+    print(f"[bench] update: {ms_per_step * 1e3:.1f} us per call on the GPU, "
+          f"{enqueue / args.steps * 1e6:.1f} us per call to enqueue on the host",
+          file=sys.stderr, flush=True)
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20

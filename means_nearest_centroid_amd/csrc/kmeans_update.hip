@@ -59,9 +59,6 @@ constexpr int kMaxRow = 512;         // bf16 values of the widest supported row
 constexpr int kStageBytes = 32768;
 constexpr int kStagePieces = kStageBytes / 16 / kReduceThreads;
 constexpr int kMaxChunk = 240;        // keeps a reduce workgroup within 40 KiB of LDS
-// Runs are handed to waves by the stripe of positions they start in: 32
-// positions, so a 128-position chunk gives every wave a stripe.
-constexpr int kStripe = 32;
 
 __device__ __forceinline__ int sort_key(int32_t label, int K) {
     return (label < 0 || label >= K) ? K : label;
@@ -473,8 +470,8 @@ __device__ __forceinline__ RowBits<V> lds_row_bits(const uint16_t *p) {
 // Chunks of P sorted positions; workgroup b takes chunks b, b + G, ... (G
 // workgroups, four per CU).  A chunk's keys, point indices and rows are
 // staged in LDS (all row loads of a chunk in flight at once), then each
-// wave takes the runs of equal keys that start in its 32-position stripes
-// (stripe s -> wave s % 4) and sums each run's rows from LDS in position
+// wave takes every fourth run of equal keys (in position order: runs w, w +
+// 4, ... go to wave w) and sums each run's rows from LDS in position
 // order.  Loads run ahead of the sums: while chunk c is summed, the rows of
 // the next chunk are on their way into registers and the keys of the one
 // after into registers too.
@@ -588,14 +585,20 @@ void upd_reduce_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
         const int c0 = c * P;
         const int n = min(N - c0, P);
         const int *sk = skey[b];
-        for (int st = wave; st * kStripe < n; st += kReduceThreads / 64) {
-            const int j = st * kStripe + lane;
+        // Every wave walks all run starts of the chunk in order and takes
+        // runs 0, 4, 8, ... (wave 0), 1, 5, ... (wave 1) and so on.
+        static_assert(((kReduceThreads / 64) & (kReduceThreads / 64 - 1)) == 0,
+                      "wave count must be a power of two");
+        int run = 0;
+        for (int base = 0; base < n; base += 64) {
+            const int j = base + lane;
             const int kj = j < n ? sk[j] : K;
-            uint64_t starts = __ballot(lane < kStripe && j < n && kj < K &&
-                                       (j == 0 || sk[j - 1] != kj));
+            uint64_t starts = __ballot(j < n && kj < K && (j == 0 || sk[j - 1] != kj));
             while (starts) {
-                const int a = st * kStripe + __builtin_ctzll(starts);
+                const int a = base + __builtin_ctzll(starts);
                 starts &= starts - 1;
+                if ((run++ & (kReduceThreads / 64 - 1)) != wave)
+                    continue;
                 const int k = __builtin_amdgcn_readfirstlane(sk[a]);
                 int e = n;
                 for (int base = a + 1; base < n; base += 64) {

@@ -196,8 +196,9 @@ kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *
  * pool, in stream order, behind the calls already queued on `stream`.  Call
  * it before destroying a stream that was passed to those entry points (a new
  * stream could otherwise inherit the buffer while the old stream's calls
- * still run), or to give the memory back.  No-op when the stream holds
- * none; KMEANS_ERR_HIP if the free fails.
+ * still run), or to give the memory back.  hipStreamPerThread gets one
+ * buffer per calling thread (release it from that thread).  No-op when the
+ * stream holds none; KMEANS_ERR_HIP if the free fails.
  */
 kmeans_status_t kmeans_release_workspace(hipStream_t stream);
 

@@ -6,7 +6,10 @@
 #include <atomic>
 #include <map>
 #include <mutex>
+#include <functional>
 #include <string>
+#include <thread>
+#include <tuple>
 #include <utility>
 
 #include "kmeans_internal.h"
@@ -52,12 +55,21 @@ int device_compute_units() {
 }
 
 namespace {
-// (device, stream) -> (buffer, bytes).  Never destroyed: at process exit the
-// runtime may be gone before static destructors run, and it reclaims device
-// memory itself.
+// (device, stream, thread) -> (buffer, bytes).  The thread is part of the key
+// only for hipStreamPerThread, one handle that names a different stream in
+// every thread.  Never destroyed: at process exit the runtime may be gone
+// before static destructors run, and it reclaims device memory itself.
+using WsKey = std::tuple<int, uintptr_t, size_t>;
 std::mutex g_ws_mutex;
-auto *g_ws = new std::map<std::pair<int, uintptr_t>, std::pair<void *, size_t>>();
+auto *g_ws = new std::map<WsKey, std::pair<void *, size_t>>();
 constexpr size_t kWorkspaceGranule = size_t(1) << 20;
+
+WsKey ws_key(int dev, hipStream_t stream) {
+    const size_t thread = stream == hipStreamPerThread
+                              ? std::hash<std::thread::id>()(std::this_thread::get_id())
+                              : 0;
+    return WsKey{dev, reinterpret_cast<uintptr_t>(stream), thread};
+}
 }  // namespace
 
 WorkspaceLease::WorkspaceLease(hipStream_t stream, size_t bytes) {
@@ -66,7 +78,7 @@ WorkspaceLease::WorkspaceLease(hipStream_t stream, size_t bytes) {
     error_ = hipGetDevice(&dev);
     if (error_ != hipSuccess)
         return;
-    auto &slot = (*g_ws)[{dev, reinterpret_cast<uintptr_t>(stream)}];
+    auto &slot = (*g_ws)[ws_key(dev, stream)];
     if (slot.second < bytes) {
         if (slot.first != nullptr) {
             void *old = slot.first;
@@ -95,7 +107,7 @@ hipError_t release_workspace(hipStream_t stream) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return e;
-    auto it = g_ws->find({dev, reinterpret_cast<uintptr_t>(stream)});
+    auto it = g_ws->find(ws_key(dev, stream));
     if (it == g_ws->end())
         return hipSuccess;
     void *p = it->second.first;

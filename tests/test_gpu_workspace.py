@@ -180,3 +180,53 @@ def test_release_is_a_no_op_without_a_buffer_and_calls_work_after_it():
     km.kmeans_release_workspace(s)
     km.kmeans_release_workspace(s)            # twice: the second finds nothing
     s.synchronize()
+
+
+def test_per_thread_default_stream_gets_a_buffer_per_thread():
+    """hipStreamPerThread is one handle naming a different stream in every
+    thread: each thread must get its own buffer, or concurrent calls from
+    two threads would share one."""
+    import ctypes
+    lib = km.load_library()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
+    per_thread = ctypes.c_void_p(2)          # hipStreamPerThread
+    sets = [inputs(N, D, K, 950 + i) for i, (N, D, K, _) in enumerate(SHAPES[:2])]
+    want = [direct(s[3], s[4], s[5]) for s in sets]
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def work(t):
+        try:
+            outs = []
+            for rep in range(6):
+                j = (t + rep) % 2
+                x = sets[j]
+                N, D, K = x[3].shape[0], x[3].shape[1], x[4].shape[0]
+                lab = torch.empty(N, dtype=torch.int32, device="cuda")
+                md = torch.empty(N, dtype=torch.float32, device="cuda")
+                torch.cuda.current_stream().synchronize()   # outputs allocated
+                st = lib.kmeans_assign_path(
+                    ctypes.c_void_p(x[3].data_ptr()), ctypes.c_void_p(x[4].data_ptr()),
+                    ctypes.c_void_p(x[5].data_ptr()), N, D, K, ctypes.c_void_p(lab.data_ptr()),
+                    ctypes.c_void_p(md.data_ptr()), km.PATH_SPLIT, SHAPES[j][3], per_thread)
+                assert st == 0, lib.kmeans_last_error()
+                outs.append((j, lab, md))
+            assert hip.hipStreamSynchronize(per_thread) == 0
+            results[t] = [(j, lab.cpu().numpy(), md.cpu().numpy()) for j, lab, md in outs]
+            assert lib.kmeans_release_workspace(per_thread) == 0
+            assert hip.hipStreamSynchronize(per_thread) == 0
+        except Exception as e:   # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=100)
+    assert not errors, errors
+    assert sorted(results) == [0, 1, 2, 3]
+    for outs in results.values():
+        for j, lab, md in outs:
+            assert np.array_equal(lab, want[j][0])
+            assert md.tobytes() == want[j][1].tobytes()

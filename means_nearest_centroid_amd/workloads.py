@@ -29,7 +29,7 @@ import numpy as np
 SEEDS = (17, 29, 43)
 
 #: The five workloads: tiny, large-K/small-D, headline, large-N/large-D,
-#: adversarial.  Index 0 is unused so that ``CONFIGS[i]`` matches "config i".
+#: adversarial.  Index 0 is unused so that workload i is ``CONFIGS[i]``.
 CONFIGS = {
     1: dict(N=4096, D=64, K=256, adversarial=False,
             name="tiny N=4096 D=64 K=256"),

@@ -95,9 +95,35 @@ void upd_hist_kernel(const int32_t *__restrict__ keys_in, int N, int K, int shif
     const int beg = t << tile_log2;
     const int fin = static_cast<int>(min(static_cast<int64_t>(N),
                                          static_cast<int64_t>(beg) + (int64_t(1) << tile_log2)));
-    for (int i = beg + tid; i < fin; i += kSortThreads) {
-        const int key = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
-        atomicAdd(&h[(key >> shift) & mask], 1);
+    // Eight keys per thread are loaded before any is counted, so their loads
+    // are in flight together (a load-then-count loop waits for each load in
+    // turn).  The loads are unconditional, clamped to the tile's last key
+    // (every launched tile holds at least one), and an empty asm takes all
+    // eight values on every lane, so that the compiler cannot sink each load
+    // into a branch of its own (where it would wait for it); positions are
+    // counted from beg, so none can wrap around 2^31.
+    constexpr int kBatch = 8;
+    const int len = fin - beg;
+    for (int rel0 = 0; rel0 < len; rel0 += kBatch * kSortThreads) {
+        int v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = keys_in[beg + min(rel0 + u * kSortThreads + tid, len - 1)];
+#if defined(__HIP_DEVICE_COMPILE__)
+        static_assert(kBatch == 8, "the asm below names eight values");
+        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),
+                          "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+#endif
+        int key[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int rel = rel0 + u * kSortThreads + tid;
+            key[u] = rel < len ? (FIRST ? sort_key(v[u], K) : v[u]) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (key[u] >= 0)
+                atomicAdd(&h[(key[u] >> shift) & mask], 1);
     }
     __syncthreads();
     int32_t *row = hist + static_cast<size_t>(tid) * stride;
@@ -226,19 +252,33 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
     const int len = fin - beg;
     // Keys and values are loaded kBatchRounds rounds at a time, all loads of
     // a batch in flight together; the first batch is issued before the
-    // offsets are worked out, so the two sets of loads overlap.
+    // offsets are worked out, so the two sets of loads overlap.  The loads
+    // are unconditional (clamped to the tile's last position) and their
+    // values are taken by an empty asm only where they are first needed, so
+    // that the compiler cannot sink each load into a branch of its own and
+    // wait for it there.
     int bkey[kBatchRounds], bval[kBatchRounds];
     auto load_batch = [&](int rel0) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < kBatchRounds; ++r) {
-            const int rel = rel0 + r * kScatterThreads + tid;
-            bkey[r] = 0;
-            bval[r] = 0;
-            if (rel < len) {
-                const int i = beg + rel;
-                bkey[r] = FIRST ? sort_key(keys_in[i], K) : keys_in[i];
-                bval[r] = FIRST ? i : vals_in[i];
-            }
+            const int i = beg + min(rel0 + r * kScatterThreads + tid, len - 1);
+            bkey[r] = keys_in[i];
+            bval[r] = FIRST ? i : vals_in[i];
+        }
+    };
+    auto ready_batch = [&](int rel0) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        static_assert(kBatchRounds == 4, "the asm below names four values");
+        asm volatile("" : "+v"(bkey[0]), "+v"(bkey[1]), "+v"(bkey[2]), "+v"(bkey[3]));
+        if constexpr (!FIRST)
+            asm volatile("" : "+v"(bval[0]), "+v"(bval[1]), "+v"(bval[2]), "+v"(bval[3]));
+#endif
+#pragma unroll
+        for (int r = 0; r < kBatchRounds; ++r) {
+            const bool in = rel0 + r * kScatterThreads + tid < len;
+            const int key = FIRST ? sort_key(bkey[r], K) : bkey[r];
+            bkey[r] = in ? key : 0;
+            bval[r] = in ? bval[r] : 0;
         }
     };
     load_batch(0);
@@ -257,12 +297,28 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
         const int qq = tid >> 8;
         const bool live = d <= min(mask, K >> shift);
         constexpr int kG = kFusedScanTiles / 16;        // 16-byte groups per quarter
-        const i4 *rv = reinterpret_cast<const i4 *>(hist + static_cast<size_t>(d) * stride) +
-                       qq * kG;
+        // One branch around all of a thread's loads (a dead row, or a quarter
+        // wholly past the row's end, loads nothing), none inside it, so that
+        // they stay in flight together: a group past the end of a partly
+        // filled quarter re-reads the row's last group and counts as zero.
+        const i4 *rv = reinterpret_cast<const i4 *>(hist + static_cast<size_t>(d) * stride);
         i4 v[kG];
 #pragma unroll
         for (int g = 0; g < kG; ++g)
-            v[g] = live && (qq * kG + g) * 4 < stride ? rv[g] : i4{0, 0, 0, 0};
+            v[g] = i4{0, 0, 0, 0};
+        if (live && qq * kG * 4 < stride) {
+#pragma unroll
+            for (int g = 0; g < kG; ++g)
+                v[g] = rv[min(qq * kG + g, stride / 4 - 1)];
+        }
+#if defined(__HIP_DEVICE_COMPILE__)
+        static_assert(kG == 8, "the asm below names eight values");
+        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),
+                          "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+#endif
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+            v[g] = live && (qq * kG + g) * 4 < stride ? v[g] : i4{0, 0, 0, 0};
         int pre = 0, tot = 0;
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
@@ -305,6 +361,7 @@ void upd_scatter_kernel(const int32_t *__restrict__ keys_in, const int32_t *__re
     for (int rel0 = 0; rel0 < len; rel0 += kBatchRounds * kScatterThreads) {
         if (rel0 != 0)
             load_batch(rel0);
+        ready_batch(rel0);
 #pragma unroll
         for (int r = 0; r < kBatchRounds; ++r) {
             const int base = rel0 + r * kScatterThreads;

@@ -45,12 +45,11 @@ def load(path: str = LIBRARY):
                                   f64p, f64p, f64p]
     lib.oracle_score_for.argtypes = [u16p, u16p, i64, i64, i32p, f64p]
     lib.oracle_sqdist_for.argtypes = [u16p, u16p, i64, i64, i32p, f64p]
-    lib.oracle_all_scores.argtypes = [u16p, u16p, i64, i64, i64, f64p]
     i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
     lib.oracle_update.argtypes = [u16p, i32p, u16p, i64, i64, i64, i64p, f64p, u16p]
     lib.oracle_bf16_from_double_array.argtypes = [f64p, i64, u16p]
     for f in ("oracle_centroid_norms", "oracle_assign", "oracle_score_for",
-              "oracle_sqdist_for", "oracle_all_scores", "oracle_update",
+              "oracle_sqdist_for", "oracle_update",
               "oracle_bf16_from_double_array"):
         getattr(lib, f).restype = None
     return lib
@@ -115,14 +114,6 @@ def sqdist_for(X, C, labels, lib=None) -> np.ndarray:
     labels = np.ascontiguousarray(labels, dtype=np.int32)
     out = np.empty(X.shape[0], dtype=np.float64)
     (lib or _get()).oracle_sqdist_for(X, C, X.shape[0], X.shape[1], labels, out)
-    return out
-
-
-def all_scores(X, C, lib=None) -> np.ndarray:
-    """fp64 score matrix ``[N][K]`` (small inputs only)."""
-    X, C = _bits(X), _bits(C)
-    out = np.empty((X.shape[0], C.shape[0]), dtype=np.float64)
-    (lib or _get()).oracle_all_scores(X, C, X.shape[0], X.shape[1], C.shape[0], out)
     return out
 
 

@@ -188,24 +188,6 @@ void oracle_sqdist_for(const uint16_t *X, const uint16_t *C, int64_t N, int64_t 
     }
 }
 
-/* Every score s_ik, row-major [N][K] (small inputs only). */
-void oracle_all_scores(const uint16_t *X, const uint16_t *C, int64_t N, int64_t D,
-                       int64_t K, double *S)
-{
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < N; ++i) {
-        for (int64_t k = 0; k < K; ++k) {
-            double n = 0.0, dot = 0.0;
-            for (int64_t j = 0; j < D; ++j) {
-                double c = widen_bf16(C[k * D + j]);
-                n += c * c;
-                dot += widen_bf16(X[i * D + j]) * c;
-            }
-            S[i * K + k] = n - 2.0 * dot;
-        }
-    }
-}
-
 /* ------------------------------------------------------------------------
  * Centroid update (the step of a Lloyd iteration that follows assignment).
  *

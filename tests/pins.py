@@ -85,6 +85,52 @@ def pin_bruteforce(lib):
                 assert _rel_close(ref["second"][i] + float(xx[i]), d2nd[i]), "runner-up wrong"
 
 
+def pin_score_and_sqdist_for(lib):
+    """The checker helpers: ``score_for`` and ``sqdist_for`` for EVERY
+    (point, centroid) pair of the tiny cases against exact rationals, with
+    the score taken from the distance form (s_ik = ||x - c_k||^2 - ||x||^2,
+    an identity, not the oracle's expanded formula), plus one random label
+    per point so a helper that reads the wrong point's label fails; and the
+    IEEE classes of non-finite cases, derived by hand."""
+    rng = np.random.default_rng(8)
+    for X, C in tiny_cases():
+        N, K = X.shape[0], C.shape[0]
+        Xe = [_exact(r) for r in X]
+        Ce = [_exact(r) for r in C]
+        dist = [[sum((a - b) * (a - b) for a, b in zip(x, c)) for c in Ce] for x in Xe]
+        xx = [sum(a * a for a in x) for x in Xe]
+        label_sets = [np.full(N, k, np.int32) for k in range(K)]
+        label_sets.append(rng.integers(0, K, N).astype(np.int32))
+        for lab in label_sets:
+            s = oracle.score_for(X, C, lab, lib=lib)
+            d = oracle.sqdist_for(X, C, lab, lib=lib)
+            for i in range(N):
+                k = int(lab[i])
+                assert _rel_close(d[i], dist[i][k]), "sqdist_for differs from exact"
+                assert _rel_close(s[i], dist[i][k] - xx[i]), "score_for differs from exact"
+    # Non-finite: +inf at j against c_kj > 0 scores -inf (distance +inf); a
+    # NaN coordinate makes both NaN; -0.0 coordinates change nothing.
+    X, C, _ = W.gaussian_mixture(4, 16, 6, 19)
+    Cf = W.bf16_bits_to_f32(C).astype(np.float64)
+    k_pos = int(np.flatnonzero(Cf[:, 3] > 0)[0])
+    k_neg = int(np.flatnonzero(Cf[:, 3] < 0)[0])
+    Xn = X.copy()
+    Xn[0, 3] = W.BF16_PINF
+    Xn[1, 3] = W.BF16_PINF
+    Xn[2, 5] = W.BF16_QNAN
+    Xn[3, ::2] = W.BF16_NZERO
+    lab = np.array([k_pos, k_neg, 0, 2], np.int32)
+    s = oracle.score_for(Xn, C, lab, lib=lib)
+    d = oracle.sqdist_for(Xn, C, lab, lib=lib)
+    assert s[0] == -np.inf and d[0] == np.inf, "+inf against a positive coordinate"
+    assert s[1] == np.inf and d[1] == np.inf, "+inf against a negative coordinate"
+    assert np.isnan(s[2]) and np.isnan(d[2]), "NaN coordinate"
+    Xp = Xn[3:4].copy()
+    Xp[0, ::2] = W.BF16_PZERO
+    assert s[3] == oracle.score_for(Xp, C, lab[3:], lib=lib)[0], "signed zero score"
+    assert d[3] == oracle.sqdist_for(Xp, C, lab[3:], lib=lib)[0], "signed zero distance"
+
+
 def pin_centroid_norms(lib):
     """n_k equals the exact rational sum of squares."""
     for _, C in tiny_cases():
@@ -390,7 +436,7 @@ def pin_update_closed_forms(lib):
     assert np.array_equal(r0["C_new"], C) and not r0["counts"].any(), "no points"
 
 
-ALL_PINS = (pin_bruteforce, pin_centroid_norms, pin_permutation,
+ALL_PINS = (pin_bruteforce, pin_score_and_sqdist_for, pin_centroid_norms, pin_permutation,
             pin_duplicates_and_equal, pin_scaling, pin_exact_member,
             pin_zero_point, pin_one_dimensional, pin_dyadic_ties,
             pin_nonfinite, pin_single_centroid, pin_bf16_rounding,

@@ -37,6 +37,22 @@ MUTANTS = [
     ("runner_up_not_tracked", "                    sec = b;\n", ""),
     ("norm_not_squared", "            n += c * c;\n        }\n        norms[k] = n;",
      "            n += c;\n        }\n        norms[k] = n;"),
+    # the checker helpers (score of a given label, distance to a given label)
+    ("score_for_dropped_norm", "        s[i] = n - 2.0 * dot;", "        s[i] = -2.0 * dot;"),
+    ("score_for_wrong_sign", "        s[i] = n - 2.0 * dot;", "        s[i] = n + 2.0 * dot;"),
+    ("score_for_norm_not_squared", "            n += c * c;\n            dot +=",
+     "            n += c;\n            dot +="),
+    ("score_for_wrong_row",
+     "const uint16_t *cr = C + (int64_t)labels[i] * D;\n        double n = 0.0, dot = 0.0;",
+     "const uint16_t *cr = C + (int64_t)labels[i > 0 ? i - 1 : 0] * D;\n"
+     "        double n = 0.0, dot = 0.0;"),
+    ("sqdist_for_wrong_row",
+     "const uint16_t *cr = C + (int64_t)labels[i] * D;\n        double d = 0.0;",
+     "const uint16_t *cr = C + (int64_t)labels[0] * D;\n        double d = 0.0;"),
+    ("sqdist_for_not_squared", "            d += e * e;\n        }\n        dist[i] = d;",
+     "            d += fabs(e);\n        }\n        dist[i] = d;"),
+    ("sqdist_for_wrong_element", "double e = widen_bf16(xr[j]) - widen_bf16(cr[j]);",
+     "double e = widen_bf16(xr[j]) - widen_bf16(C[j + labels[i]]);"),
     # centroid update and its bf16 rounding
     ("mean_over_all_points", "means[k * D + j] /= (double)counts[k];",
      "means[k * D + j] /= (double)N;"),

@@ -12,7 +12,8 @@
  * Euclidean one,
  *
  *     s_ik = ||c_k||^2 - 2 x_i . c_k ,   label_i = lowest k minimising s_ik,
- *     min_dist_i = ||x_i - c_label_i||^2   (computed as ||x_i||^2 + s_best).
+ *     min_dist_i = ||x_i - c_label_i||^2   (summed directly over the
+ *                                          coordinates, in fp32).
  *
  * Non-finite inputs: scores follow IEEE arithmetic and are ranked
  * -inf < finite < +inf < NaN with ties to the lower index, so a NaN score
@@ -97,7 +98,8 @@ kmeans_status_t kmeans_centroid_norms(const void *C, int64_t K, int64_t D,
  *             KMEANS_PATH_DIRECT then returns KMEANS_ERR_UNSUPPORTED).
  *   labels    int32 [N], written: lowest index minimising s_ik.
  *   min_dist  fp32 [N], written: squared distance to the chosen centroid,
- *             max(0, ||x||^2 + s_best) for finite data.
+ *             sum_j (x_j - c_j)^2 in fp32 (not ||x||^2 + s_best, which
+ *             cancels when the data lie far from the origin).
  *
  * Small-N / large-K shapes run a K-split path whose scratch (8 bytes per
  * point per split + 4 bytes per point) is the stream's workspace (see

@@ -113,6 +113,20 @@ def _matrix(t, name):
     return t
 
 
+def _vector(t, name, dtype, n, device):
+    """Check a caller-supplied 1-D output (or input) tensor: the C ABI sees
+    only a pointer, so a wrong dtype, a short tensor or a strided view would
+    be written out of bounds without an error."""
+    import torch
+    if (not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda
+            or t.device != device or t.numel() != n or not t.is_contiguous()):
+        got = (f"{t.dtype}, {tuple(t.shape)}, {t.device}, contiguous={t.is_contiguous()}"
+               if isinstance(t, torch.Tensor) else type(t).__name__)
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {n} elements "
+                         f"on {device} (got {got})")
+    return t
+
+
 def abi_version() -> int:
     return load_library().kmeans_abi_version()
 
@@ -134,6 +148,7 @@ def kmeans_centroid_norms(C, norms=None, stream=None):
     K, D = C.shape
     if norms is None:
         norms = torch.empty(K, dtype=torch.float32, device=C.device)
+    _vector(norms, "norms", torch.float32, K, C.device)
     lib = load_library()
     _check(lib, lib.kmeans_centroid_norms(_ptr(C), K, D, _ptr(norms), _stream_handle(stream)))
     return norms
@@ -147,13 +162,15 @@ def _assign_args(X, C, norms, labels, min_dist):
     K = C.shape[0]
     if C.shape[1] != D:
         raise ValueError(f"X has D={D} but C has D={C.shape[1]}")
-    if (not isinstance(norms, torch.Tensor) or norms.dtype != torch.float32
-            or not norms.is_cuda or norms.numel() != K or not norms.is_contiguous()):
-        raise ValueError("norms must be a contiguous fp32 CUDA tensor of K elements")
+    if C.device != X.device:
+        raise ValueError(f"X is on {X.device} but C on {C.device}")
+    _vector(norms, "norms", torch.float32, K, X.device)
     if labels is None:
         labels = torch.empty(N, dtype=torch.int32, device=X.device)
     if min_dist is None:
         min_dist = torch.empty(N, dtype=torch.float32, device=X.device)
+    _vector(labels, "labels", torch.int32, N, X.device)
+    _vector(min_dist, "min_dist", torch.float32, N, X.device)
     return X, C, norms, N, D, K, labels, min_dist
 
 
@@ -192,10 +209,10 @@ def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=N
     K = C_old.shape[0]
     if C_old.shape[1] != D:
         raise ValueError(f"X has D={D} but C_old has D={C_old.shape[1]}")
-    if (not isinstance(labels, torch.Tensor) or labels.dtype != torch.int32
-            or not labels.is_cuda or labels.numel() != N or not labels.is_contiguous()):
-        raise ValueError("labels must be a contiguous int32 CUDA tensor of N elements")
+    if C_old.device != X.device:
+        raise ValueError(f"X is on {X.device} but C_old on {C_old.device}")
     dev = C_old.device
+    _vector(labels, "labels", torch.int32, N, dev)
     if C_new is None:
         C_new = torch.empty_like(C_old)
     else:
@@ -208,11 +225,12 @@ def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=N
         counts = torch.empty(K, dtype=torch.int32, device=dev)
     if means is None and with_means:
         means = torch.empty((K, D), dtype=torch.float32, device=dev)
+    if C_new.device != dev:
+        raise ValueError(f"C_new must be on {dev}")
     for t, name, dt, n in ((norms, "norms", torch.float32, K), (counts, "counts", torch.int32, K),
                            (means, "means", torch.float32, K * D)):
-        if t is not None and (t.dtype != dt or not t.is_cuda or t.numel() != n
-                              or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor of {n} elements")
+        if t is not None:
+            _vector(t, name, dt, n, dev)
     lib = load_library()
     _check(lib, lib.kmeans_update(_ptr(X), _ptr(labels), _ptr(C_old), N, D, K, _ptr(C_new),
                                   _ptr(norms), _ptr(counts), _ptr(means),

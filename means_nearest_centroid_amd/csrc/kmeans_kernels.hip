@@ -118,53 +118,97 @@ __device__ __forceinline__ float point_lane_sum(float x) {
     return __uint_as_float(u) + __uint_as_float(w);
 }
 
+// min(a, b) of two running bests (never NaN: they start at +inf and take
+// only NaN-ignoring minima) as one v_min_f32; fminf would first quiet each
+// operand with a v_max, which values that come from a lane exchange need.
+__device__ __forceinline__ float min_of_finite_or_inf(uint32_t a, uint32_t b) {
+    float r;
+    asm volatile("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // (s, i) strictly before (so, io) under score-then-index order.
 __device__ __forceinline__ bool pair_before(float s, int32_t i, float so, int32_t io) {
     return s < so || (s == so && i < io);
 }
 
-// Final label and min_dist of point n from its merged winner (s, lab) and
-// ||x||^2.  Hot case: finite result, min_dist = max(0, xx + s).  Cold cases
-// (non-finite data) recompute on the VALU in IEEE fp32; only the class of
-// each score matters there and it does not depend on summation order.
-__device__ void finalize_point(int n, float s, int32_t lab, float xx,
+// Final label and min_dist of point n from its merged winner `lab` and the
+// squared distance d to that centroid, which the caller sums directly from
+// the point's and the centroid's coordinates (||x||^2 + s would cancel badly
+// when ||x||^2 is much larger than the distance, e.g. for data far from the
+// origin).  Cold case: no finite or -inf score won (every score +inf or NaN):
+// lowest +inf index, else 0 -- found by a VALU rescan in IEEE fp32, where only
+// each score's class matters, which does not depend on summation order.
+__device__ void finalize_point(int n, int32_t lab, float xx, float d,
                                const uint16_t *__restrict__ X,
                                const uint16_t *__restrict__ C,
                                const float *__restrict__ norms, int D, int K,
                                int32_t *__restrict__ labels,
                                float *__restrict__ min_dist) {
-    float md;
-    if (lab == kNoLabel || !isfinite(xx) || !isfinite(s)) {
+    if (lab == kNoLabel) {
         const uint16_t *xr = X + static_cast<size_t>(n) * D;
-        if (lab == kNoLabel) {
-            // Every score is +inf or NaN: lowest +inf index, else 0.  A NaN
-            // coordinate makes every score NaN.
-            lab = 0;
-            if (!isnan(xx)) {
-                for (int k = 0; k < K; ++k) {
-                    const uint16_t *cr = C + static_cast<size_t>(k) * D;
-                    float sk = norms[k];
-                    for (int j = 0; j < D; ++j)
-                        sk = fmaf(-2.0f * widen(xr[j]), widen(cr[j]), sk);
-                    if (sk == INFINITY) {
-                        lab = k;
-                        break;
-                    }
+        // A NaN coordinate (NaN ||x||^2) makes every score NaN: label 0.
+        lab = 0;
+        if (!isnan(xx)) {
+            for (int k = 0; k < K; ++k) {
+                const uint16_t *cr = C + static_cast<size_t>(k) * D;
+                float sk = norms[k];
+                for (int j = 0; j < D; ++j)
+                    sk = fmaf(-2.0f * widen(xr[j]), widen(cr[j]), sk);
+                if (sk == INFINITY) {
+                    lab = k;
+                    break;
                 }
             }
         }
         const uint16_t *cr = C + static_cast<size_t>(lab) * D;
-        float d = 0.0f;
+        d = 0.0f;
         for (int j = 0; j < D; ++j) {
             const float e = widen(xr[j]) - widen(cr[j]);
             d = fmaf(e, e, d);
         }
-        md = d;
-    } else {
-        md = fmaxf(0.0f, xx + s);
     }
     labels[n] = lab;
-    min_dist[n] = md;
+    min_dist[n] = d;
+}
+
+// Whether the winner's squared distance may be taken as the expansion
+// d = max(0, ||x||^2 + s) for a point with squared norm xx, at padded width
+// 16 * ks.  Its fp32 rounding error grows with ||x||^2 (and ||c||^2, which
+// is close to it for a point near its centroid) while the tolerance on d is
+// 2e-3 (d + 1): with a typical error of about 2^-24 sqrt(D + 40) (||x||^2 +
+// ||c||^2) for the D-term sums behind xx and s, the expansion is used while
+// ||x||^2 <= R (d + 1), R = 2e-3 / (4 * 4 * 2^-24 * sqrt(D + 40)) (a quarter
+// of the tolerance at ||c||^2 up to 3 ||x||^2), so it stays about 8x inside
+// the tolerance (R = 162 at D = 128; points of zero-mean data sit near 50).
+// Beyond it (data far from the origin) the distance is summed directly.
+// NaN or infinite xx or d fail the test and take the direct sum too.  R per
+// padded width (2097.152 / sqrt(16 ks + 40), rounded down), a compile-time
+// constant shared by the assign and merge kernels, so both decide alike.
+constexpr float expansion_ratio(int ks) {
+    return ks <= 1 ? 280.0f : ks == 2 ? 247.0f : ks == 4 ? 205.0f
+         : ks == 8 ? 161.0f : ks == 16 ? 121.0f : 89.0f;
+}
+__device__ __forceinline__ bool expansion_accurate(float xx, float d, int ks) {
+    return xx <= expansion_ratio(ks) * (d + 1.0f);
+}
+
+// d + sum (x_e - c_e)^2 over the 8 coordinates of one 16-byte chunk, the
+// point held as -2x (so x = -0.5 * that, exactly, and the fma below is the
+// correctly rounded x - c), in coordinate order.
+__device__ __forceinline__ float sqdiff_chunk(u32x4 xneg2, u32x4 c, float d) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float xl = __uint_as_float(xneg2[w] << 16);
+        const float xh = __uint_as_float(xneg2[w] & 0xffff0000u);
+        const float cl = __uint_as_float(c[w] << 16);
+        const float ch = __uint_as_float(c[w] & 0xffff0000u);
+        const float el = fmaf(-0.5f, xl, -cl);
+        const float eh = fmaf(-0.5f, xh, -ch);
+        d = fmaf(el, el, d);
+        d = fmaf(eh, eh, d);
+    }
+    return d;
 }
 
 // Raw buffer resource over `bytes` bytes at `base`: loads past the end
@@ -395,6 +439,11 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     constexpr int DMA_PER_WAVE = STAGE_BYTES / (1024 * WAVES);
     static_assert(STAGE_BYTES % (1024 * WAVES) == 0, "block must split into 1 KiB DMAs");
     static_assert(BK % kTileRows == 0 && BK <= 64 * WAVES, "block shape");
+    // Centroid blocks per best-sharing period: about 8 tiles (256 rows).  A
+    // CPU count over the headline workload's scores puts the search branch
+    // at 0.64 of (point block, tile) steps without sharing, 0.32 with a share
+    // every 8 tiles and 0.30 with one every tile.
+    constexpr int SHARE_BLOCKS = TB >= 8 ? 1 : 8 / TB;
 
     __shared__ __attribute__((aligned(16))) uint8_t c_st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t c_st1[STAGE_BYTES];
@@ -494,10 +543,35 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         bt[p] = kNoLabel;
         bo[p] = 0;
     }
+    // The lanes that hold one point (64 / G of them, each seeing a quarter or
+    // a half of every tile's rows) take the point's running best as their own
+    // threshold.  A lane whose best is beaten by another lane's drops its
+    // record (tile kNoLabel, which loses every tie in the final merge) and
+    // keeps only the threshold, so it searches for a slot only when it finds
+    // a score below the point's best, not merely below its own: the search
+    // branch is taken about half as often.  Exact and tie-safe: a lane
+    // holding the point's best keeps its record, and everything found after
+    // the exchange lies in later tiles (higher indices), where a strict '<'
+    // against an equal threshold leaves the earlier record in place.
+    auto share_best = [&](int p) KM_INLINE {
+        float pb = bs[p];
+        uint32_t u, w;
+        if constexpr (G == 16) {
+            lane_pair<16>(__float_as_uint(pb), u, w);
+            pb = min_of_finite_or_inf(u, w);
+        }
+        lane_pair<32>(__float_as_uint(pb), u, w);
+        pb = min_of_finite_or_inf(u, w);
+        bt[p] = pb < bs[p] ? kNoLabel : bt[p];
+        bs[p] = pb;
+    };
     // Fold the scores of point block p in v (centroid kt + the element's tile
     // row, as the lowest_row_of_min_* helpers map it, + 4*kq) into that
-    // block's running best.
-    auto reduce = [&](int p, const accv (&v)[MB], int kt) KM_INLINE {
+    // block's running best; first share the best between the point's lanes
+    // when `share` (wave-uniform).
+    auto reduce = [&](int p, const accv (&v)[MB], int kt, bool share) KM_INLINE {
+        if (share)
+            share_best(p);
         // Running minimum over the scores in pairs; t[k] after pair k.
         float t[MB * AV / 2];
         float mn = bs[p];
@@ -535,7 +609,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     constexpr int NACC = PB > 1 ? PB : (KS <= 8 ? 2 : 1);
     static_assert(NACC != 2 || PB > 1 || TB % 2 == 0, "tile parity must repeat in every block");
     accv acc[NACC][MB];
-    if (NACC > 1) {
+    if constexpr (NACC > 1) {
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -552,7 +626,11 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     // current operands (a, ninit), whose registers are refilled with the next
     // tile's fragments right after their last use, interleaved with the
     // reductions.
-    auto tile = [&](const uint8_t *next_c, const float *next_n, int next_r0, int kt, int j) KM_INLINE {
+    // `share`: wave-uniform, true when this tile's block starts a sharing
+    // period; the best is shared right before each point block folds the
+    // period's first tile.
+    auto tile = [&](const uint8_t *next_c, const float *next_n, int next_r0, int kt, int j,
+                    bool share) KM_INLINE {
 #pragma unroll
         for (int p = 0; p < PB; ++p) {
             accv (&dst)[MB] = acc[PB > 1 ? p : (NACC == 2 ? (j & 1) : 0)];
@@ -571,13 +649,13 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                 }
             }
             if (NACC == 1)
-                reduce(0, acc[0], kt);
+                reduce(0, acc[0], kt, share && j == 0);
             else if (PB == 1)
-                reduce(0, acc[(j + 1) & 1], kt - kTileRows);
+                reduce(0, acc[(j + 1) & 1], kt - kTileRows, share && j == 1);
             else if (p == 0)
-                reduce(PB - 1, acc[PB - 1], kt - kTileRows);
+                reduce(PB - 1, acc[PB - 1], kt - kTileRows, share && j == 1);
             else
-                reduce(p - 1, acc[p - 1], kt);
+                reduce(p - 1, acc[p - 1], kt, share && j == 0);
         }
     };
 
@@ -630,10 +708,11 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     // into cc/nc once the barrier shows nobody reads block b any more.
     auto do_block = [&](int b, uint8_t *cc, float *nc, uint8_t *cn, float *nn) KM_INLINE {
         const int kb = k_begin + b * BK;
+        const bool share = b % SHARE_BLOCKS == 0;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
             if (j + 1 < TB) {
-                tile(cc, nc, (j + 1) * kTileRows, kb + j * kTileRows, j);
+                tile(cc, nc, (j + 1) * kTileRows, kb + j * kTileRows, j, share);
             } else {
                 if (b + 1 < nblocks) {
                     write_norm(nn);
@@ -644,7 +723,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
                         load_norm(b + 2);
                     }
                 }
-                tile(cn, nn, 0, kb + j * kTileRows, j);
+                tile(cn, nn, 0, kb + j * kTileRows, j, share);
             }
         }
     };
@@ -654,11 +733,13 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
             break;
         do_block(b + 1, c_st1, n_st1, c_st0, n_st0);
     }
-    if (NACC > 1)   // the last tile's last point block
+    if constexpr (NACC > 1)   // the last tile's last point block
         reduce(PB - 1, acc[PB > 1 ? PB - 1 : ((TB - 1) & 1)],
-               k_begin + (nblocks - 1) * BK + (TB - 1) * kTileRows);
+               k_begin + (nblocks - 1) * BK + (TB - 1) * kTileRows, false);
 
     // ---- merge the lanes that hold the same point ----
+    int32_t lab[PB];
+    float win[PB];
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
         float s = bs[p];
@@ -675,27 +756,96 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         if constexpr (G == 16)
             merge(std::integral_constant<int, 16>{});
         merge(std::integral_constant<int, 32>{});
-        const int n = wg_point0 + wave * P * kTileCols + p * G + pcol;
-        if (kq == 0 && n < N) {
-            if (write_partials) {
-                ws_score[static_cast<size_t>(split) * N + n] = s;
-                ws_label[static_cast<size_t>(split) * N + n] = i;
+        win[p] = s;
+        lab[p] = i;
+    }
+    if (write_partials) {
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+            const int n = wg_point0 + wave * P * kTileCols + p * G + pcol;
+            if (kq == 0 && n < N) {
+                ws_score[static_cast<size_t>(split) * N + n] = win[p];
+                ws_label[static_cast<size_t>(split) * N + n] = lab[p];
                 if (split == 0)
                     ws_xx[n] = xx[p];
-            } else {
-                finalize_point(n, s, i, xx[p], X, C, norms, D, K, labels, min_dist);
             }
         }
+        return;
+    }
+    // ---- min_dist ----
+    // The expansion ||x||^2 + s where it is accurate; otherwise (data far
+    // from the origin, or non-finite) the sum of (x - c)^2 over the winner's
+    // row, for every point of the wave if any of them needs it.
+    float dist[PB];
+    bool need_any = false;
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+        dist[p] = fmaxf(0.0f, xx[p] + win[p]);
+        need_any |= lab[p] != kNoLabel && !expansion_accurate(xx[p], dist[p], KS);
+    }
+    if (__any(need_any)) {
+        // The packed -2x registers are read again here; made opaque, so
+        // that the compiler does not keep their unpacked fp32 halves (which
+        // it can see are the prologue's products) alive through the K loop.
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                asm volatile("" : "+v"(xb[p][ks]));
+        // The winners' rows, all loads in flight together (global loads:
+        // each lane has its own row, which a buffer resource, being
+        // wave-uniform, cannot address without a loop over the distinct
+        // rows).  kNoLabel reads row 0 (the cold path recomputes);
+        // padding columns are zero.
+        u32x4 cw[PB][NKS];
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+            const uint16_t *row = C + static_cast<size_t>(lab[p] == kNoLabel ? 0 : lab[p]) * D;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int c0 = ks * KSTEP + kq * 8;
+                cw[p][ks] = c0 < D ? *reinterpret_cast<const u32x4 *>(row + c0)
+                                   : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        // Each lane of a point adds up the coordinates it holds (its 8-wide
+        // chunk of every k-step, in order), then the point's lanes combine
+        // as point_lane_sum does; merge_kernel repeats exactly this order
+        // and this choice, so the direct and split paths give the same bits.
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+            float d = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                d = sqdiff_chunk(xb[p][ks], cw[p][ks], d);
+            d = point_lane_sum<G>(d);
+            if (!expansion_accurate(xx[p], dist[p], KS))
+                dist[p] = d;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+        const int n = wg_point0 + wave * P * kTileCols + p * G + pcol;
+        if (kq == 0 && n < N)
+            finalize_point(n, lab[p], xx[p], dist[p], X, C, norms, D, K, labels, min_dist);
     }
 }
 
-// Second pass of the K-split path: (score, index) minimum over the splits.
+// Second pass of the K-split path: (score, index) minimum over the splits,
+// then the winner's squared distance summed in the order the assign kernel
+// uses for the geometry G of this D (lane q of a point adds its 8-wide
+// chunks q*8, q*8 + KSTEP, ...; the lanes' sums combine pairwise), so split
+// and direct outputs are bitwise equal.
+template <int KS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void merge_kernel(const float *__restrict__ ws_score, const int32_t *__restrict__ ws_label,
                   const float *__restrict__ ws_xx, int splits,
                   const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
                   const float *__restrict__ norms, int N, int D, int K,
                   int32_t *__restrict__ labels, float *__restrict__ min_dist) {
+    constexpr int G = mfma_geometry(KS);
+    constexpr int KSTEP = G == 32 ? 16 : 32;
+    constexpr int LANES = 64 / G;
     const int n = blockIdx.x * kThreads + threadIdx.x;
     if (n >= N)
         return;
@@ -709,7 +859,27 @@ void merge_kernel(const float *__restrict__ ws_score, const int32_t *__restrict_
             i = io;
         }
     }
-    finalize_point(n, s, i, ws_xx[n], X, C, norms, D, K, labels, min_dist);
+    const float xx = ws_xx[n];
+    float d = fmaxf(0.0f, xx + s);
+    if (i != kNoLabel && !expansion_accurate(xx, d, KS)) {
+        const uint16_t *xr = X + static_cast<size_t>(n) * D;
+        const uint16_t *cr = C + static_cast<size_t>(i) * D;
+        float part[LANES];
+#pragma unroll
+        for (int q = 0; q < LANES; ++q) {
+            part[q] = 0.0f;
+            for (int c0 = q * 8; c0 < D; c0 += KSTEP)
+                for (int e = 0; e < 8; ++e) {
+                    const float diff = widen(xr[c0 + e]) - widen(cr[c0 + e]);
+                    part[q] = fmaf(diff, diff, part[q]);
+                }
+        }
+        if constexpr (LANES == 4)
+            d = (part[0] + part[1]) + (part[2] + part[3]);
+        else
+            d = part[0] + part[1];
+    }
+    finalize_point(n, i, xx, d, X, C, norms, D, K, labels, min_dist);
 }
 
 // ||c_k||^2: 16 lanes per row, 16 rows per workgroup, 16-byte loads.  Every
@@ -782,8 +952,19 @@ hipError_t launch_merge(const Plan &pl, const uint16_t *X, const uint16_t *C,
                         float *min_dist, const float *ws_score, const int32_t *ws_label,
                         const float *ws_xx, hipStream_t stream) {
     const int blocks = (N + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(kThreads), 0, stream, ws_score,
-                       ws_label, ws_xx, pl.splits, X, C, norms, N, D, K, labels, min_dist);
+#define KM_MERGE(KSV)                                                                       \
+    hipLaunchKernelGGL(merge_kernel<KSV>, dim3(blocks), dim3(kThreads), 0, stream, ws_score, \
+                       ws_label, ws_xx, pl.splits, X, C, norms, N, D, K, labels, min_dist)
+    switch (pl.ks) {
+    case 1: KM_MERGE(1); break;
+    case 2: KM_MERGE(2); break;
+    case 4: KM_MERGE(4); break;
+    case 8: KM_MERGE(8); break;
+    case 16: KM_MERGE(16); break;
+    case 32: KM_MERGE(32); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef KM_MERGE
     return hipGetLastError();
 }
 

@@ -123,9 +123,28 @@ def test_sweep_shape_sampled(N, D, K, seed):
     parity.check(X, C, lab, md, idx=parity.sample_indices(N, seed, 2048, 512, 64))
 
 
-@pytest.fixture(scope="module")
-def workload5():
-    X, C, meta = W.make_config(5, 17)
+# Every point of the sweep shapes whose dispatch no workload covers: the
+# K-split path with four ranges (65536 x 64 x 16384, every seed) and the
+# wide direct path at N = 1M, D = 128 (seed 17).
+FULL_SWEEP_CASES = [(65536, 64, 16384, s) for s in W.SEEDS] + [(1048576, 128, 4096, 17)]
+
+
+@pytest.mark.parametrize("N,D,K,seed", FULL_SWEEP_CASES,
+                         ids=[f"{n}x{d}x{k}-s{s}" for n, d, k, s in FULL_SWEEP_CASES])
+def test_sweep_shape_every_point(N, D, K, seed):
+    X, C, _ = W.gaussian_mixture(N, D, K, seed)
+    plan = km.kmeans_plan(N, D, K, torch.cuda.get_device_properties(0).multi_processor_count)
+    if N == 65536:
+        assert plan["path"] == km.PATH_SPLIT and plan["splits"] == 4, plan
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md)
+
+
+@pytest.fixture(scope="module", params=W.SEEDS, ids=[f"s{s}" for s in W.SEEDS])
+def workload5(request):
+    """The adversarial workload at each of the three seeds (generated and
+    assigned once per seed; the tests below run per seed)."""
+    X, C, meta = W.make_config(5, request.param)
     lab, md = run(X, C)
     return X, C, meta, lab, md
 
@@ -420,3 +439,66 @@ def test_api_errors_on_device_tensors():
     with pytest.raises(km.KmeansError) as e:
         km.kmeans_centroid_norms(Cw)
     assert e.value.status == km.KMEANS_ERR_UNSUPPORTED
+
+
+def test_output_tensors_are_validated_before_any_launch():
+    """The C ABI sees only pointers, so the binding checks every caller-given
+    output (and the norms) before the call: a wrong dtype, a short tensor, a
+    strided view or another device raises ValueError and nothing is written."""
+    X = dev(W.gaussian_mixture(100, 64, 10, 96)[0])
+    C = dev(W.gaussian_mixture(1, 64, 10, 96)[1])
+    n = km.kmeans_centroid_norms(C)
+    N = X.shape[0]
+    good_lab = torch.full((N,), -7, dtype=torch.int32, device="cuda")
+    good_md = torch.full((N,), -7.0, dtype=torch.float32, device="cuda")
+    bad_outputs = [
+        dict(labels=torch.full((N,), -7, dtype=torch.int64, device="cuda")),
+        dict(labels=torch.full((N - 1,), -7, dtype=torch.int32, device="cuda")),
+        dict(labels=torch.full((2 * N,), -7, dtype=torch.int32, device="cuda")[::2]),
+        dict(labels=torch.full((N,), -7, dtype=torch.int32)),
+        dict(min_dist=torch.full((N,), -7.0, dtype=torch.float64, device="cuda")),
+        dict(min_dist=torch.full((N - 3,), -7.0, dtype=torch.float32, device="cuda")),
+    ]
+    for bad in bad_outputs:
+        kw = dict(labels=good_lab, min_dist=good_md)
+        kw.update(bad)
+        with pytest.raises(ValueError):
+            km.kmeans_assign(X, C, n, **kw)
+        with pytest.raises(ValueError):
+            km.kmeans_assign_path(X, C, n, km.PATH_SPLIT, 2, **kw)
+        torch.cuda.synchronize()
+        for t in bad.values():
+            assert bool((t == -7).all()), "an output was written before the check"
+    assert bool((good_lab == -7).all()) and bool((good_md == -7.0).all())
+    for bad_n in (n[:-1], n.double(), torch.cat([n, n])[::2], n.cpu()):
+        with pytest.raises(ValueError):
+            km.kmeans_assign(X, C, bad_n)
+    short = torch.full((9,), -7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        km.kmeans_centroid_norms(C, norms=short)
+    torch.cuda.synchronize()
+    assert bool((short == -7.0).all())
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("offset", [1.5, 2.5, 10.0, 30.0, 200.0])
+def test_data_far_from_origin(offset, D):
+    """Half of the coordinates shifted by `offset`: ||x||^2 is then tens to
+    millions of times the distance to the nearest centroid, so a distance
+    formed as ||x||^2 + score loses accuracy as the shift grows; the kernel
+    sums (x - c)^2 directly past a ratio that depends on D, and min_dist must
+    meet the acceptance rule on both sides of that switch (the small shifts
+    sit just below and just above it).  Split must equal direct bit for bit."""
+    rng = np.random.default_rng(int(offset * 10) + D)
+    N, K = 6000, 300
+    mu = rng.standard_normal((K, D), dtype=np.float32)
+    shift = np.zeros(D, np.float32)
+    shift[::2] = offset
+    a = rng.integers(0, K, N)
+    X = W.f32_to_bf16_bits(mu[a] + shift + 0.1 * rng.standard_normal((N, D), dtype=np.float32))
+    C = W.f32_to_bf16_bits(mu + shift + 0.05 * rng.standard_normal((K, D), dtype=np.float32))
+    lab, md = run(X, C)
+    st = parity.check(X, C, lab, md)
+    assert st["bad_dist"] == 0
+    ls, ms = run(X, C, km.PATH_SPLIT, 3)
+    assert np.array_equal(lab, ls) and md.tobytes() == ms.tobytes()

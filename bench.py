@@ -16,7 +16,11 @@ duration measured by HIP events on the launch stream.  ``mfma_ceiling`` is
 the rate of the same MFMA issued back to back on this workload's operand
 values (no memory, no epilogue): what the matrix pipe sustains on this data,
 against which ``roofline.achieved`` is also read.  ``cpu_baseline`` times the
-CPU oracle on a bounded sample of the same workload.
+CPU oracle on a bounded sample of the same workload; the same leg checks the
+outputs of the timed calls against the oracle (``parity``: the last timed
+call on each seeded set, on the points that oracle run covered for the first
+set and the first 2048 points of the others) and exits non-zero, after
+printing the line, if any point fails the acceptance rule.
 """
 
 from __future__ import annotations
@@ -338,22 +342,70 @@ def measure_sclk(step, n_steps: int, step_ms: float, dev):
     return {x: float(np.mean(v)) for x, v in sorted(by_xcd.items())}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(X, C, target_s: float):
     """Time the oracle on the first points of the workload, growing the
-    sample until one run takes about ``target_s`` seconds."""
+    sample until one run takes about ``target_s`` seconds.  Returns the
+    baseline record and the oracle's result for the sample (the parity check
+    of the timed outputs reuses it)."""
     import oracle
     n = 64
     while True:
         t0 = time.perf_counter()
-        oracle.assign(X[:n], C)
+        ref = oracle.assign(X[:n], C)
         dt = time.perf_counter() - t0
         if dt >= target_s or n >= X.shape[0]:
             break
         grow = max(2.0, min(16.0, 1.2 * target_s / max(dt, 1e-3)))
         n = min(X.shape[0], int(n * grow))
-    return dict(value=n / dt, unit="points/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"first {n} points of seed {W.SEEDS[0]}, all {C.shape[0]} "
-                       f"centroids, fp64, {dt:.2f} s wall")
+    rec = dict(value=n / dt, unit="points/s", cores=oracle.num_threads(), kind="oracle",
+               sample=f"first {n} points of seed {W.SEEDS[0]}, all {C.shape[0]} "
+                      f"centroids, fp64, {dt:.2f} s wall",
+               cpu_model=cpu_model(),
+               build="gcc " + " ".join(oracle.BUILD_FLAGS) + " (generic x86-64)")
+    return rec, ref
+
+
+def timed_output_parity(host_sets, outputs, ref0, head: int = 2048):
+    """The acceptance rule on outputs of the timed calls: the last timed call
+    on each seeded set, checked on the first points of every set (the pages'
+    nightly comparison checks the first 2048 assignments of each seeded set,
+    "Benchmark methodology"); for the first set on every point the CPU
+    baseline's oracle run covered (``ref0``), else on the first ``head``."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import parity
+    per_seed = {}
+    total_bad = 0
+    reports = []
+    for s, ((X, C), (lab, md)) in enumerate(zip(host_sets, outputs)):
+        if s == 0 and ref0 is not None:
+            n = len(ref0["labels"])
+            ref = ref0
+        else:
+            n = min(head, X.shape[0])
+            ref = oracle.assign(X[:n], C)
+        stats, report = parity.evaluate(X, C, lab, md, idx=np.arange(n), ref=ref)
+        per_seed[str(W.SEEDS[s])] = dict(points=n, bad=stats["bad"],
+                                         strict=stats.get("strict"), near=stats.get("near"))
+        total_bad += stats["bad"]
+        if report:
+            reports.append(f"seed {W.SEEDS[s]}: {report}")
+    return dict(rule="labels exact where the oracle's top-two gap >= 1e-3(|best|+1), "
+                     "else in the near-tie set; min_dist within 2e-3(|d|+1)",
+                checked="the last timed call on each seeded set",
+                points=sum(v["points"] for v in per_seed.values()), bad=total_bad,
+                per_seed=per_seed), reports
 
 
 UPDATE_METRIC = "centroid update (Lloyd step after assignment): points/sec at N={N},D={D},K={K} (1 GPU)"
@@ -451,7 +503,9 @@ def run_update(args):
                 break
         cpu = dict(value=reps * N / dt, unit="points/s", cores=1, kind="oracle",
                    sample=f"the whole workload, {reps} calls over the three seeded sets, "
-                          f"fp64, one thread, {dt:.2f} s wall")
+                          f"fp64, one thread, {dt:.2f} s wall",
+                   cpu_model=cpu_model(),
+                   build="gcc " + " ".join(oracle.BUILD_FLAGS) + " (generic x86-64)")
     out = {
         "metric": UPDATE_METRIC.format(N=N, D=D, K=K),
         "value": N / (ms_per_step / 1e3),
@@ -475,6 +529,7 @@ def run_update(args):
                          kernel="kmeans_update (all its kernels, one call)",
                          avg_launch_us=round(avg_s * 1e6, 2), bytes_per_launch=nbytes),
         "cpu_baseline": cpu,
+        "parity": timed_parity,
         "breakdown_us": {"call_median": round(float(np.median(call_ms)) * 1e3, 2),
                          "call_min": round(float(call_ms.min()) * 1e3, 2),
                          "call_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
@@ -546,18 +601,21 @@ def main():
 
     sets = [(to_dev(X), to_dev(C)) for X, C in host_sets]
     norms = [torch.empty(K, dtype=torch.float32, device=dev) for _ in sets]
-    labels = torch.empty(N, dtype=torch.int32, device=dev)
-    min_dist = torch.empty(N, dtype=torch.float32, device=dev)
+    # One pair of output buffers per seeded set, so that after the timed
+    # region each holds the last timed call on its set (checked below).
+    labels = [torch.empty(N, dtype=torch.int32, device=dev) for _ in sets]
+    min_dist = [torch.empty(N, dtype=torch.float32, device=dev) for _ in sets]
     stream = torch.cuda.current_stream()
     plan = km.kmeans_plan(N, D, K, torch.cuda.get_device_properties(dev).multi_processor_count)
 
     def step(i, ev=None):
-        X, C = sets[i % len(sets)]
-        n = norms[i % len(sets)]
+        j = i % len(sets)
+        X, C = sets[j]
+        n = norms[j]
         km.kmeans_centroid_norms(C, n, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        km.kmeans_assign(X, C, n, labels, min_dist, stream=stream)
+        km.kmeans_assign(X, C, n, labels[j], min_dist[j], stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -591,6 +649,8 @@ def main():
     assign_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     print(f"[bench] {args.steps} steps: {total_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall",
           file=sys.stderr, flush=True)
+    # Outputs of the timed calls, before any later step overwrites them.
+    timed_outputs = [(lab.cpu().numpy(), md.cpu().numpy()) for lab, md in zip(labels, min_dist)]
 
     if args.copy_calibration_mib:
         # A plain streaming kernel of known traffic (read n bytes, write n
@@ -637,10 +697,15 @@ def main():
         ceiling["assign_frac_of_ceiling"] = round(achieved / ceiling["tflops"], 4)
 
     cpu = None
+    timed_parity = None
+    parity_reports = []
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         X0, C0 = host_sets[0]
-        cpu = cpu_baseline(X0, C0, args.cpu_seconds)
+        cpu, ref0 = cpu_baseline(X0, C0, args.cpu_seconds)
+        print("[bench] checking the timed outputs against the oracle", file=sys.stderr,
+              flush=True)
+        timed_parity, parity_reports = timed_output_parity(host_sets, timed_outputs, ref0)
 
     value = N / (ms_per_step / 1e3)
     out = {
@@ -666,6 +731,7 @@ def main():
         "mfma_ceiling": ceiling,
         "sclk": sclk,
         "cpu_baseline": cpu,
+        "parity": timed_parity,
         "breakdown_us": {
             "norms_median": round(float(np.median(norms_ms)) * 1e3, 2),
             "assign_median": round(float(np.median(assign_ms)) * 1e3, 2),
@@ -676,6 +742,10 @@ def main():
         "assign_only_points_per_s": N / (float(np.median(assign_ms)) / 1e3),
     }
     print(json.dumps(out), flush=True)
+    if parity_reports:
+        print("[bench] timed outputs FAIL the acceptance rule:\n" + "\n".join(parity_reports),
+              file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

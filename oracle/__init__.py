@@ -23,10 +23,14 @@ LIBRARY = os.path.join(_HERE, "libkmeans_oracle.so")
 _lib = None
 
 
+# gcc flags of the oracle build: generic x86-64 code (the library is built
+# on one machine and may run on another host CPU), OpenMP over points.
+BUILD_FLAGS = ("-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11")
+
+
 def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
-    """Compile the oracle with gcc (generic x86-64, OpenMP)."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           *extra_flags, source, "-o", output + ".tmp", "-lm"]
+    """Compile the oracle with gcc (BUILD_FLAGS)."""
+    cmd = ["gcc", *BUILD_FLAGS, *extra_flags, source, "-o", output + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(output + ".tmp", output)
     return output

@@ -38,6 +38,15 @@ def check(X, C, labels, min_dist, idx=None, ref=None, lowest=None):
     Returns a dict of counts; raises AssertionError listing the first bad
     points.  ``ref`` may hold a precomputed ``oracle.assign`` of ``X[idx]``.
     """
+    stats, report = evaluate(X, C, labels, min_dist, idx, ref, lowest)
+    if report:
+        raise AssertionError(f"parity failure {stats}\n" + report)
+    return stats
+
+
+def evaluate(X, C, labels, min_dist, idx=None, ref=None, lowest=None):
+    """The rule of ``check`` without raising: (counts, report of the first
+    bad points, empty when every checked point passes)."""
     labels = np.asarray(labels)
     min_dist = np.asarray(min_dist)
     if idx is None:
@@ -47,7 +56,11 @@ def check(X, C, labels, min_dist, idx=None, ref=None, lowest=None):
     gl = labels[idx].astype(np.int32)
     gd = min_dist[idx].astype(np.float64)
     K = C.shape[0]
-    assert np.all((gl >= 0) & (gl < K)), "label out of range"
+    if not np.all((gl >= 0) & (gl < K)):
+        j = int(np.flatnonzero((gl < 0) | (gl >= K))[0])
+        return (dict(points=len(idx), bad=int(((gl < 0) | (gl >= K)).sum()),
+                     label_out_of_range=True),
+                f"point {idx[j]}: label {gl[j]} out of range [0, {K})")
     if ref is None:
         ref = oracle.assign(Xs, C)
     ol, best, second = ref["labels"], ref["best"], ref["second"]
@@ -78,14 +91,13 @@ def check(X, C, labels, min_dist, idx=None, ref=None, lowest=None):
                  near_label_differs=int((near & differ).sum()),
                  bad_strict=int(bad_strict.sum()), bad_near=int(bad_near.sum()),
                  bad_dist=int(bad_dist.sum()), bad_class=int(bad_class.sum()))
-    if bad.any():
-        lines = []
-        for j in np.flatnonzero(bad)[:10]:
-            lines.append(f"point {idx[j]}: gpu=({gl[j]}, {gd[j]!r}) oracle=({ol[j]}, "
-                         f"{ref['dist'][j]!r}) best={best[j]!r} second={second[j]!r} "
-                         f"s_gpu={s_g[j]!r} d_ref={d_ref[j]!r}")
-        raise AssertionError(f"parity failure {stats}\n" + "\n".join(lines))
-    return stats
+    lines = []
+    for j in np.flatnonzero(bad)[:10]:
+        lines.append(f"point {idx[j]}: gpu=({gl[j]}, {gd[j]!r}) oracle=({ol[j]}, "
+                     f"{ref['dist'][j]!r}) best={best[j]!r} second={second[j]!r} "
+                     f"s_gpu={s_g[j]!r} d_ref={d_ref[j]!r}")
+    stats["bad"] = int(bad.sum())
+    return stats, "\n".join(lines)
 
 
 def sample_indices(N: int, seed: int = 0, head: int = 2048, rand: int = 2048, tail: int = 64):

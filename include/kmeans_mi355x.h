@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KMEANS_ABI_VERSION 4
+#define KMEANS_ABI_VERSION 5
 
 /* Supported feature dimension: 16 <= D <= 512 and D % 16 == 0. */
 #define KMEANS_MIN_D 16
@@ -109,6 +109,32 @@ kmeans_status_t kmeans_centroid_norms(const void *C, int64_t K, int64_t D,
 kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms,
                               int64_t N, int64_t D, int64_t K, int32_t *labels,
                               float *min_dist, hipStream_t stream);
+
+/*
+ * Size of the fixed device buffer that kmeans_assign_static uses for the
+ * K-split path's scratch (16 MiB, held by every device the library runs on
+ * until the process ends).
+ */
+#define KMEANS_STATIC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * kmeans_assign for callers that cannot allocate device memory during the
+ * call: code being captured into a HIP graph, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, outputs (bit for bit), dispatch and
+ * errors as kmeans_assign, but the K-split path's scratch (8 bytes per point
+ * per K-range + 4 per point) comes from a fixed device buffer of
+ * KMEANS_STATIC_SCRATCH_BYTES that the library holds per device, so the call
+ * makes no hipMalloc/hipFree or other allocating call.  The direct path needs
+ * no scratch.  A shape whose split plan needs more than the buffer returns
+ * KMEANS_ERR_UNSUPPORTED before any launch (kmeans_assign handles it).
+ * Every call on a device shares that device's buffer and leaves its contents
+ * behind: calls that overlap in time on one device (different streams or
+ * threads, without ordering between them) race and give undefined results;
+ * calls ordered on one stream are safe.
+ */
+kmeans_status_t kmeans_assign_static(const void *X, const void *C, const float *norms,
+                                     int64_t N, int64_t D, int64_t K, int32_t *labels,
+                                     float *min_dist, hipStream_t stream);
 
 /*
  * kmeans_assign with the dispatch forced: `path` as in kmeans_path_t, and

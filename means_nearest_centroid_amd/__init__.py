@@ -70,6 +70,8 @@ def load_library(path: str = LIBRARY):
     lib.kmeans_centroid_norms.restype = ctypes.c_int
     lib.kmeans_assign.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp]
     lib.kmeans_assign.restype = ctypes.c_int
+    lib.kmeans_assign_static.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.kmeans_assign_static.restype = ctypes.c_int
     lib.kmeans_assign_path.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp]
     lib.kmeans_assign_path.restype = ctypes.c_int
     lib.kmeans_plan.argtypes = [i64, i64, i64, i32, i32p, i32p, i32p, i32p, i32p, i32p]
@@ -180,6 +182,17 @@ def kmeans_assign(X, C, norms, labels=None, min_dist=None, stream=None):
     lib = load_library()
     _check(lib, lib.kmeans_assign(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
                                   _ptr(min_dist), _stream_handle(stream)))
+    return labels, min_dist
+
+
+def kmeans_assign_static(X, C, norms, labels=None, min_dist=None, stream=None):
+    """``kmeans_assign`` whose K-split scratch is the library's fixed device
+    buffer (no allocation inside the call; give ``labels`` and ``min_dist``
+    to allocate nothing at all).  Calls that overlap on one GPU race."""
+    X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
+    lib = load_library()
+    _check(lib, lib.kmeans_assign_static(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
+                                         _ptr(min_dist), _stream_handle(stream)))
     return labels, min_dist
 
 

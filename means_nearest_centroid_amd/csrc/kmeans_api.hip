@@ -19,6 +19,17 @@ namespace {
 thread_local std::string g_last_error;
 }  // namespace
 
+// ---- The fixed device scratch of kmeans_assign_static ----
+//
+// kmeans_assign_static's split path takes its scratch from this file-scope
+// device array instead of the stream's workspace, so that the call allocates
+// nothing.  Each device that the library runs on holds its own copy until
+// the process ends.  The host-side name `scratch` is only a stand-in for the
+// device symbol: its device address, per device, comes from
+// hipGetSymbolAddress (static_scratch below) and is the only form ever
+// handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[KMEANS_STATIC_SCRATCH_BYTES];
+
 namespace kmeans {
 
 kmeans_status_t fail(kmeans_status_t st, const char *fmt, ...) {
@@ -152,9 +163,59 @@ kmeans_status_t check_shape(int64_t N, int64_t D, int64_t K) {
     return KMEANS_OK;
 }
 
+constexpr size_t kStaticScratchBytes = KMEANS_STATIC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's `scratch`, resolved once per device
+// (with that device current) on the first call there.
+kmeans_status_t static_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(KMEANS_ERR_UNSUPPORTED, "device %d: the static scratch serves devices "
+                    "0..%d", dev, kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(KMEANS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s",
+                        dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KMEANS_OK;
+}
+
+enum class Scratch { kWorkspace, kStatic };
+
+// The split path's two launches with their scratch at `base`: partial scores
+// [splits][N], partial labels [splits][N], ||x||^2 [N].
+kmeans_status_t launch_split(const kmeans::Plan &pl, const uint16_t *Xb, const uint16_t *Cb,
+                             const float *norms, int n, int d, int k, int32_t *labels,
+                             float *min_dist, void *base, hipStream_t stream) {
+    const size_t per = static_cast<size_t>(n);
+    auto *ws_score = static_cast<float *>(base);
+    auto *ws_label = reinterpret_cast<int32_t *>(ws_score + per * pl.splits);
+    auto *ws_xx = reinterpret_cast<float *>(ws_label + per * pl.splits);
+    hipError_t e = kmeans::launch_assign(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score,
+                                         ws_label, ws_xx, stream);
+    if (e == hipSuccess)
+        e = kmeans::launch_merge(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score,
+                                 ws_label, ws_xx, stream);
+    if (e != hipSuccess)
+        return fail(KMEANS_ERR_HIP, "split-path launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int64_t N,
                            int64_t D, int64_t K, int32_t *labels, float *min_dist,
-                           int path, int count, hipStream_t stream) {
+                           int path, int count, hipStream_t stream,
+                           Scratch scratch_kind = Scratch::kWorkspace) {
     kmeans_status_t st = check_shape(N, D, K);
     if (st != KMEANS_OK)
         return st;
@@ -201,24 +262,29 @@ kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int
         return ok();
     }
 
-    // Split path: the stream's scratch holds the partial winners and ||x||^2.
+    // Split path: scratch for the partial winners and ||x||^2, from the
+    // stream's workspace or from the fixed device array.  Every element the
+    // merge pass reads is written by the assign pass first, so neither needs
+    // clearing.
     const size_t per = static_cast<size_t>(N);
     const size_t bytes = per * pl.splits * (sizeof(float) + sizeof(int32_t)) + per * sizeof(float);
+    void *base = nullptr;
+    if (scratch_kind == Scratch::kStatic) {
+        if (bytes > kStaticScratchBytes)
+            return fail(KMEANS_ERR_UNSUPPORTED, "N=%lld D=%lld K=%lld plans %d K-ranges, whose "
+                        "scratch (%zu bytes) exceeds the static buffer (%zu bytes); use "
+                        "kmeans_assign", static_cast<long long>(N), static_cast<long long>(D),
+                        static_cast<long long>(K), pl.splits, bytes, kStaticScratchBytes);
+        st = static_scratch(&base);
+        if (st != KMEANS_OK)
+            return st;
+        return launch_split(pl, Xb, Cb, norms, n, d, k, labels, min_dist, base, stream);
+    }
     const kmeans::WorkspaceLease lease(stream, bytes);
     if (lease.error() != hipSuccess)
         return fail(KMEANS_ERR_NO_MEMORY, "workspace of %zu bytes: %s", bytes,
                     hipGetErrorString(lease.error()));
-    auto *ws_score = static_cast<float *>(lease.ptr());
-    auto *ws_label = reinterpret_cast<int32_t *>(ws_score + per * pl.splits);
-    auto *ws_xx = reinterpret_cast<float *>(ws_label + per * pl.splits);
-    hipError_t e = kmeans::launch_assign(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score,
-                                         ws_label, ws_xx, stream);
-    if (e == hipSuccess)
-        e = kmeans::launch_merge(pl, Xb, Cb, norms, n, d, k, labels, min_dist, ws_score,
-                                 ws_label, ws_xx, stream);
-    if (e != hipSuccess)
-        return fail(KMEANS_ERR_HIP, "split-path launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return launch_split(pl, Xb, Cb, norms, n, d, k, labels, min_dist, lease.ptr(), stream);
 }
 
 }  // namespace
@@ -254,6 +320,13 @@ kmeans_status_t kmeans_assign(const void *X, const void *C, const float *norms, 
                               int64_t D, int64_t K, int32_t *labels, float *min_dist,
                               hipStream_t stream) {
     return run_assign(X, C, norms, N, D, K, labels, min_dist, KMEANS_PATH_AUTO, 0, stream);
+}
+
+kmeans_status_t kmeans_assign_static(const void *X, const void *C, const float *norms,
+                                     int64_t N, int64_t D, int64_t K, int32_t *labels,
+                                     float *min_dist, hipStream_t stream) {
+    return run_assign(X, C, norms, N, D, K, labels, min_dist, KMEANS_PATH_AUTO, 0, stream,
+                      Scratch::kStatic);
 }
 
 kmeans_status_t kmeans_assign_path(const void *X, const void *C, const float *norms,

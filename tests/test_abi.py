@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for f in ("kmeans_centroid_norms", "kmeans_assign", "kmeans_assign_path",
+    for f in ("kmeans_centroid_norms", "kmeans_assign", "kmeans_assign_static",
+              "kmeans_assign_path",
               "kmeans_plan", "kmeans_update", "kmeans_release_workspace", "kmeans_last_error",
               "kmeans_abi_version"):
         assert f in names

@@ -52,6 +52,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float widen(uint16_t b) {
@@ -535,13 +536,30 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     bf16x8 a[MB][NKS];
     accv ninit[MB];
 
+    // Where the registers allow it (one point block per wave, or the D = 512
+    // shape with a whole SIMD's registers), a lane whose best improves only
+    // saves that tile's scores and the exact slot is searched in them once,
+    // after the loop (DEFER); elsewhere the slot is searched on the spot.
+    // Either way it is the lowest row holding the best score, so the outputs
+    // are the same bits.
+    constexpr bool DEFER = (P == 1 && KS <= 8) || KS >= 32;
     float bs[PB];
     int32_t bt[PB], bo[PB];
+    accv sv[DEFER ? PB : 1][MB];
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
         bs[p] = INFINITY;
         bt[p] = kNoLabel;
         bo[p] = 0;
+    }
+    if constexpr (DEFER) {
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int r = 0; r < AV; ++r)
+                    sv[p][m][r] = INFINITY;
     }
     // The lanes that hold one point (64 / G of them, each seeing a quarter or
     // a half of every tile's rows) take the point's running best as their own
@@ -585,15 +603,54 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         const bool improved = mn < bs[p];
         bs[p] = mn;                // mn <= bs[p]: the same value when not improved
         if (improved) {
-            int slot;
-            if constexpr (G == 16)
-                slot = lowest_row_of_min_16x16(v[0], v[1], t, mn);
-            else if constexpr (KS < 32)
-                slot = lowest_row_of_min_32x32(v[0], t, mn);
-            else
-                slot = lowest_row_of_min_32x32_chain(v[0], mn);
             bt[p] = kt;
-            bo[p] = slot;
+            if constexpr (DEFER) {
+                // Only the improving lanes (exec mask) copy the tile's
+                // scores, two per v_mov_b64, where the search costs a compare
+                // and a select per pair of scores.  As assembly, so that the
+                // compiler keeps the copies inside the branch rather than
+                // turning them into a select per score on every step.
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int r = 0; r < AV; r += 2) {
+                        f32x2 d;
+                        const f32x2 src = {v[m][r], v[m][r + 1]};
+                        asm volatile("v_mov_b64 %0, %1" : "=v"(d) : "v"(src));
+                        sv[p][m][r] = d[0];
+                        sv[p][m][r + 1] = d[1];
+                    }
+            } else {
+                int slot;
+                if constexpr (G == 16)
+                    slot = lowest_row_of_min_16x16(v[0], v[1], t, mn);
+                else
+                    slot = lowest_row_of_min_32x32(v[0], t, mn);
+                bo[p] = slot;
+            }
+        }
+    };
+    // Lowest row of the saved tile whose score equals the block's best (the
+    // minimum of the saved scores whenever the record is valid).
+    auto saved_slot = [&](int p) KM_INLINE {
+        if constexpr (!DEFER) {
+            return bo[p];
+        } else if constexpr (G == 32 && KS >= 32) {
+            return lowest_row_of_min_32x32_chain(sv[p][0], bs[p]);
+        } else {
+            float t[MB * AV / 2];
+            float mn = INFINITY;
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int r = 0; r < AV; r += 2) {
+                    mn = __builtin_fminf(__builtin_fminf(mn, sv[p][m][r]), sv[p][m][r + 1]);
+                    t[(m * AV + r) / 2] = mn;
+                }
+            if constexpr (G == 16)
+                return lowest_row_of_min_16x16(sv[p][0], sv[p][1], t, bs[p]);
+            else
+                return lowest_row_of_min_32x32(sv[p][0], t, bs[p]);
         }
     };
 
@@ -743,7 +800,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
         float s = bs[p];
-        int32_t i = bt[p] == kNoLabel ? kNoLabel : bt[p] + bo[p] + 4 * kq;
+        int32_t i = bt[p] == kNoLabel ? kNoLabel : bt[p] + saved_slot(p) + 4 * kq;
         auto merge = [&](auto off) KM_INLINE {
             uint32_t su, sw, iu, iw;
             lane_pair<decltype(off)::value>(__float_as_uint(s), su, sw);

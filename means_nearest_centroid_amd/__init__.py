@@ -20,7 +20,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(_HERE, "libkmeans_mi355x.so")
+# The built library; KMEANS_MI355X_LIBRARY names another build of the same
+# sources instead (the host-sanitizer test loads one built with AddressSanitizer).
+LIBRARY = os.environ.get("KMEANS_MI355X_LIBRARY") or os.path.join(_HERE, "libkmeans_mi355x.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "kmeans_mi355x.h")
 
 KMEANS_OK = 0

@@ -94,7 +94,8 @@ def _counter_per_dispatch(csv_path: str, counter: str):
     """Per kernel kind (assign, merge, calibration copy, and the update's
     kernels together), the counter's total over all dispatches and the number
     of dispatches, from a rocprofv3 --pmc counter_collection.csv; for the
-    update, the dispatches of its finish kernel (one per call)."""
+    update, the dispatches of its last kernel (one per call: the finish kernel
+    of the sort path or the bucket kernel)."""
     import csv
     import collections
     tot = collections.defaultdict(float)
@@ -108,7 +109,7 @@ def _counter_per_dispatch(csv_path: str, counter: str):
             if kind is None:
                 continue
             tot[kind] += float(row["Counter_Value"])
-            if kind != "update" or "upd_finish_kernel" in name:
+            if kind != "update" or "upd_finish_kernel" in name or "upd_bucket_kernel" in name:
                 disp[kind].add(row["Dispatch_Id"])
     return {k: tot[k] / len(disp[k]) for k in tot}
 
@@ -441,14 +442,16 @@ def run_update(args):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     sets = [(to_dev(X), torch.from_numpy(lab).to(dev), to_dev(C)) for X, C, lab in host]
-    C_new = torch.empty((K, D), dtype=torch.bfloat16, device=dev)
-    norms = torch.empty(K, dtype=torch.float32, device=dev)
-    counts = torch.empty(K, dtype=torch.int32, device=dev)
+    # Outputs per set, so the last timed call on each set can be checked.
+    outs = [(torch.empty((K, D), dtype=torch.bfloat16, device=dev),
+             torch.empty(K, dtype=torch.float32, device=dev),
+             torch.empty(K, dtype=torch.int32, device=dev)) for _ in sets]
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
         X, lab, C = sets[i % len(sets)]
-        km.kmeans_update(X, lab, C, C_new, norms, counts, stream=stream)
+        C_new, norms, counts = outs[i % len(sets)]
+        km.kmeans_update(X, lab, C, C_new, norms, counts, stream=stream, path=args.update_path)
         if ev is not None:
             ev.record(stream)
 
@@ -484,11 +487,14 @@ def run_update(args):
         torch.neg(a, out=b)
         torch.cuda.synchronize()
 
+    timed = [(o[0].view(torch.int16).cpu().numpy().view(np.uint16), o[1].cpu().numpy(),
+              o[2].cpu().numpy()) for o in outs]
     nbytes = update_bytes(N, D, K)
     avg_s = float(call_ms.mean()) / 1e3
     achieved = nbytes / avg_s / 1e9
     traffic = traffic_record(args.config, "update")
     cpu = None
+    timed_parity, bad_sets = None, []
     if args.cpu_seconds > 0:
         import oracle
         # The whole workload takes the oracle well under a second: repeat it
@@ -506,6 +512,21 @@ def run_update(args):
                           f"fp64, one thread, {dt:.2f} s wall",
                    cpu_model=cpu_model(),
                    build="gcc " + " ".join(oracle.BUILD_FLAGS) + " (generic x86-64)")
+        # The acceptance rule on the last timed call of every seeded set.
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import parity
+        per_seed, bad_sets = {}, []
+        for si, ((X0, C0, l0), (cn, nr, ct)) in enumerate(zip(host, timed)):
+            try:
+                st = parity.check_update(X0, l0, C0, cn, nr, ct)
+                per_seed[str(W.SEEDS[si])] = dict(clusters=st["clusters"], ok=True)
+            except AssertionError as e:
+                per_seed[str(W.SEEDS[si])] = dict(ok=False)
+                bad_sets.append(f"seed {W.SEEDS[si]}: {e}")
+        timed_parity = dict(rule="counts exact, empty rows unchanged, bf16 rows within the "
+                                 "fp32 summation bound of the oracle's mean, norms of the rows",
+                            checked="the last timed call on each seeded set, every cluster",
+                            bad_sets=len(bad_sets), per_seed=per_seed)
     out = {
         "metric": UPDATE_METRIC.format(N=N, D=D, K=K),
         "value": N / (ms_per_step / 1e3),
@@ -522,7 +543,8 @@ def run_update(args):
         "config": {"workload": f"centroid update, {cfg['name']}, bf16 Gaussian mixture, labels "
                                f"= generating centres, seeds {list(W.SEEDS)} rotated",
                    "N": N, "D": D, "K": K, "settle_ms": args.settle_ms,
-                   "settle_steps": settled},
+                   "settle_steps": settled,
+                   "path": {0: "automatic", 1: "sort", 2: "buckets"}[args.update_path]},
         "roofline": dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                          unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                          traffic=(traffic["hbm_bytes_per_launch"] if traffic else None),
@@ -535,6 +557,10 @@ def run_update(args):
                          "call_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
     }
     print(json.dumps(out), flush=True)
+    if bad_sets:
+        print("[bench] update parity FAILED on the timed outputs:\n" + "\n".join(bad_sets),
+              file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 def main():
@@ -557,6 +583,8 @@ def main():
     ap.add_argument("--record-command", default="", help="command stored with the record")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the MFMA-only probe (mfma_ceiling: null)")
+    ap.add_argument("--update-path", type=int, default=0, choices=(0, 1, 2),
+                    help="with --update: 0 automatic, 1 the radix-sort path, 2 the bucket path")
     ap.add_argument("--update", action="store_true",
                     help="time kmeans_update (the Lloyd step after assignment) on the "
                          "workload instead (one JSON line)")

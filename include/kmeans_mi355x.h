@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KMEANS_ABI_VERSION 5
+#define KMEANS_ABI_VERSION 6
 
 /* Supported feature dimension: 16 <= D <= 512 and D % 16 == 0. */
 #define KMEANS_MIN_D 16
@@ -200,17 +200,51 @@ kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_uni
  *   means   fp32 [K][D] or NULL (then not written); an empty cluster's row
  *           is its old centroid widened to fp32.
  *
- * The sums are fp32, each in an order fixed by the data (points grouped by
- * label in index order, in chunks of 128 sorted positions whose partial sums
- * add in chunk order), so the outputs are bitwise deterministic; IEEE
- * arithmetic throughout (a NaN coordinate makes that coordinate of the mean
- * NaN).  Scratch of about 16 bytes per point plus 8 bytes per cluster is
- * the stream's workspace (see kmeans_release_workspace); KMEANS_ERR_NO_MEMORY
- * if it cannot grow.
+ * The sums are fp32, each in an order fixed by the data (see
+ * kmeans_update_path for the two orders), so the outputs are bitwise
+ * deterministic for a given path; IEEE arithmetic throughout (a NaN
+ * coordinate makes that coordinate of the mean NaN).  Scratch of at most
+ * about 16 bytes per point plus 8 bytes per cluster is the stream's
+ * workspace (see kmeans_release_workspace); KMEANS_ERR_NO_MEMORY if it
+ * cannot grow.  The path is chosen from the shape (kmeans_update_path with
+ * KMEANS_UPDATE_AUTO): buckets when 256 <= K <= 4096 and N <= 2^24,
+ * else
+ * the radix sort.
  */
 kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
                               int64_t N, int64_t D, int64_t K, void *C_new, float *norms,
                               int32_t *counts, float *means, hipStream_t stream);
+
+typedef enum {
+    KMEANS_UPDATE_AUTO = 0,
+    /* Stable LSD radix sort of the labels (8-bit digits or fewer), then
+     * fixed chunks of 128 sorted positions (32 KiB of rows) summed per run
+     * of equal labels; a cluster cut by chunk edges adds its partial sums in
+     * chunk order.  Any N and K; a cluster of any size is spread over many
+     * workgroups.  Per radix pass a histogram and a scatter launch (and a
+     * scan launch when N is over 2^21), then the reduce and the finish. */
+    KMEANS_UPDATE_SORT = 1,
+    /* Clusters grouped into at most 1024 buckets of 1, 2 or 4 clusters;
+     * each tile of 512 or more points sorts its own points by bucket,
+     * stably, and records where each bucket starts in it; then one
+     * workgroup per bucket gathers its points tile by tile and sums their
+     * rows in index order (four waves each sum a fixed quarter of every 512
+     * points, added in wave order).  Two launches.  N <= 2^24 and K <= 4096
+     * (else KMEANS_ERR_UNSUPPORTED); a bucket holding a large share of all
+     * points runs on one compute unit, far slower than the sort path. */
+    KMEANS_UPDATE_BUCKETS = 2
+} kmeans_update_path_t;
+
+/*
+ * kmeans_update with the path forced (kmeans_update_path_t; any other value
+ * is KMEANS_ERR_INVALID_ARG).  Same arguments, outputs and errors
+ * otherwise.  The two paths sum in different orders, so their means may
+ * differ in the last bits; each is deterministic.
+ */
+kmeans_status_t kmeans_update_path(const void *X, const int32_t *labels, const void *C_old,
+                                   int64_t N, int64_t D, int64_t K, void *C_new, float *norms,
+                                   int32_t *counts, float *means, int32_t path,
+                                   hipStream_t stream);
 
 /*
  * The workspace of `stream` on the current device.  kmeans_assign's K-split

@@ -35,6 +35,10 @@ KMEANS_ERR_NO_MEMORY = 5
 PATH_AUTO = 0
 PATH_DIRECT = 1
 PATH_SPLIT = 2
+# kmeans_update_path_t
+UPDATE_AUTO = 0
+UPDATE_SORT = 1
+UPDATE_BUCKETS = 2
 
 _STATUS_NAMES = {
     0: "KMEANS_OK", 1: "KMEANS_ERR_INVALID_ARG", 2: "KMEANS_ERR_UNSUPPORTED",
@@ -80,6 +84,8 @@ def load_library(path: str = LIBRARY):
     lib.kmeans_plan.restype = ctypes.c_int
     lib.kmeans_update.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.kmeans_update.restype = ctypes.c_int
+    lib.kmeans_update_path.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    lib.kmeans_update_path.restype = ctypes.c_int
     lib.kmeans_release_workspace.argtypes = [vp]
     lib.kmeans_release_workspace.restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
@@ -212,11 +218,12 @@ def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, count: int = 0,
 
 
 def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=None,
-                  with_means: bool = False, stream=None):
+                  with_means: bool = False, stream=None, path: int = UPDATE_AUTO):
     """Centroid update from ``labels``: ``(C_new bf16 [K, D], norms fp32 [K],
     counts int32 [K], means fp32 [K, D] or None)``.  An empty cluster keeps
     its row of ``C_old``; labels outside ``[0, K)`` count for no cluster.
-    ``C_new`` may be ``C_old`` itself (in-place update)."""
+    ``C_new`` may be ``C_old`` itself (in-place update).  ``path``:
+    ``UPDATE_AUTO``, ``UPDATE_SORT`` or ``UPDATE_BUCKETS`` (kmeans_update_path)."""
     import torch
     X = _matrix(X, "X")
     C_old = _matrix(C_old, "C_old")
@@ -247,9 +254,9 @@ def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=N
         if t is not None:
             _vector(t, name, dt, n, dev)
     lib = load_library()
-    _check(lib, lib.kmeans_update(_ptr(X), _ptr(labels), _ptr(C_old), N, D, K, _ptr(C_new),
-                                  _ptr(norms), _ptr(counts), _ptr(means),
-                                  _stream_handle(stream)))
+    _check(lib, lib.kmeans_update_path(_ptr(X), _ptr(labels), _ptr(C_old), N, D, K,
+                                       _ptr(C_new), _ptr(norms), _ptr(counts), _ptr(means),
+                                       int(path), _stream_handle(stream)))
     return C_new, norms, counts, means
 
 

@@ -755,6 +755,423 @@ void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__rest
     }
 }
 
+// ---- 4. bucket path: a tile-local sort and one workgroup per bucket ------
+//
+// For K up to 4096 and N up to 2^24 (the common Lloyd shapes), two launches
+// replace the radix passes, the reduce and the finish kernels.  Clusters are
+// grouped into nb <= 1024 buckets of S = 2^s clusters (bucket k >> s).
+//
+//  a. upd_bin_kernel: every tile of 2^tl points sorts its own points by
+//     bucket, stably (index order inside a bucket), and records where each
+//     bucket starts in the tile (dir[tile][bucket]).  No global offsets: a
+//     bucket's points are the concatenation, over tiles in order, of one
+//     segment per tile, which is already index order.
+//  b. upd_bucket_kernel: one workgroup per bucket walks those segments in
+//     tile order, in chunks of 512 slots; each of its four waves sums a fixed
+//     quarter of every chunk's slots in order into per-cluster registers, the
+//     four partials are added in wave order, and the workgroup finishes its S
+//     clusters (empty ones keep their rows).  The order of every sum depends
+//     only on the data, so a call gives the same bits every time.
+//
+// A bucket is summed by one workgroup, so a bucket holding a large share of
+// all points runs on one CU (correct, but far slower than the radix path,
+// whose reduce spreads any cluster over fixed chunks).
+
+constexpr int kBinThreads = 256;     // 4 waves; each owns a quarter of the tile
+constexpr int kBinWaves = kBinThreads / 64;
+constexpr int kMaxBuckets = 1024;
+constexpr int kBinDigitsPerThread = kMaxBuckets / kBinThreads;   // 4: one 16-byte group
+constexpr int kMaxBinTiles = 1024;
+constexpr int64_t kMaxBinPoints = int64_t(1) << 24;
+constexpr int kMaxBucketLog2 = 2;    // S <= 4
+constexpr int64_t kMaxBinClusters = int64_t(kMaxBuckets) << kMaxBucketLog2;
+constexpr int kBucketThreads = 256;  // 4 waves
+constexpr int kBucketWaves = kBucketThreads / 64;
+constexpr int kBucketChunk = 512;    // slots resolved per round
+
+// Tile t: positions [t << tl, min(N, (t + 1) << tl)).  Wave w owns the
+// contiguous quarter [w q, (w + 1) q) of the tile (q = 2^tl / 4), so the
+// stable order is: bucket, then wave, then position inside the wave.
+//  1. per-wave bucket counts (LDS atomics on the wave's own row; stray
+//     labels are not counted);
+//  2. one exclusive scan over (bucket, wave), bucket-major: cnt[w][d]
+//     becomes the first slot of (w, d), and dir[t][d] the first slot of
+//     bucket d, dir[t][nb] the number of points with a real label.  Thread
+//     r owns buckets 4r .. 4r + 3 (one 16-byte group per row);
+//  3. each wave ranks its points 64 at a time in position order: lanes with
+//     the same bucket are found with one ballot per bucket bit, a lane's
+//     slot is the running slot of its bucket plus the earlier such lanes, and
+//     the group's last lane advances the running slot.  The label and index
+//     of every point with a real label are written at its slot.
+// Labels are loaded eight chunks (512 points) per wave at a time, all in
+// flight together (unconditional loads clamped to the wave's last point,
+// taken by an empty asm); a wave holding one batch (tiles up to 2048) keeps
+// it in registers from the counts to the ranks.
+__global__ __launch_bounds__(kBinThreads)
+void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2, int nb,
+                    int tl, int32_t *__restrict__ skey, int32_t *__restrict__ sidx,
+                    int32_t *__restrict__ dir) {
+    typedef int32_t i4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) int cnt[kBinWaves * kMaxBuckets];
+    __shared__ int wtot[kBinWaves];
+    constexpr int kBatch = 8;
+    constexpr int NR = kMaxBuckets;                // row length of cnt
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int t = blockIdx.x;
+    const int beg = t << tl;                       // N <= 2^24: no overflow
+    const int len = min(N - beg, 1 << tl);
+    const int q = (1 << tl) / kBinWaves;
+    const int wb = min(len, w * q);
+    const int we = min(len, wb + q);
+    i4 *cv = reinterpret_cast<i4 *>(cnt);
+#pragma unroll
+    for (int r = 0; r < kBinWaves; ++r)
+        cv[r * (NR / 4) + tid] = i4{0, 0, 0, 0};
+    int v[kBatch];
+    auto load_batch = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = labels[beg + min(i0 + u * 64 + lane, we - 1)];
+#if defined(__HIP_DEVICE_COMPILE__)
+        static_assert(kBatch == 8, "the asm below names eight values");
+        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),
+                          "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+#endif
+    };
+    // Bucket of a label, nb for a stray one.
+    auto bucket = [&](int32_t l) __attribute__((always_inline)) {
+        return (l < 0 || l >= K) ? nb : (l >> s_log2);
+    };
+    const bool one_batch = we - wb <= kBatch * 64;
+    if (wb < we)
+        load_batch(wb);
+    __syncthreads();                               // cnt cleared
+    int *mine = cnt + w * NR;
+
+    // 1. Counts.
+    for (int i0 = wb; i0 < we; i0 += kBatch * 64) {
+        if (i0 != wb)
+            load_batch(i0);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int d = bucket(v[u]);
+            if (i0 + u * 64 + lane < we && d < nb)
+                atomicAdd(&mine[d], 1);
+        }
+    }
+    __syncthreads();
+
+    // 2. Scan.
+    {
+        i4 c[kBinWaves];
+#pragma unroll
+        for (int r = 0; r < kBinWaves; ++r)
+            c[r] = cv[r * (NR / 4) + tid];
+        int tot[kBinDigitsPerThread];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kBinDigitsPerThread; ++j) {
+            tot[j] = c[0][j] + c[1][j] + c[2][j] + c[3][j];
+            sum += tot[j];
+        }
+        int x = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off)
+                x += y;
+        }
+        if (lane == 63)
+            wtot[w] = x;
+        __syncthreads();
+        int ex = x - sum;
+        for (int v2 = 0; v2 < w; ++v2)
+            ex += wtot[v2];
+        int32_t *drow = dir + static_cast<size_t>(t) * (nb + 1);
+        i4 o[kBinWaves];
+#pragma unroll
+        for (int j = 0; j < kBinDigitsPerThread; ++j) {
+            const int d = tid * kBinDigitsPerThread + j;
+            if (d <= nb)
+                drow[d] = ex;
+            int run = ex;
+#pragma unroll
+            for (int r = 0; r < kBinWaves; ++r) {
+                o[r][j] = run;
+                run += c[r][j];
+            }
+            ex += tot[j];
+        }
+        if (tid == kBinThreads - 1 && nb == kMaxBuckets)
+            drow[nb] = ex;                         // the total (no owner at index 1024)
+#pragma unroll
+        for (int r = 0; r < kBinWaves; ++r)
+            cv[r * (NR / 4) + tid] = o[r];
+    }
+    __syncthreads();
+
+    // 3. Ranks and placement.  Every lane of the wave reads its bucket's
+    // running slot before the group's last lane writes it back (LDS runs a
+    // wave's operations in order, and the leader's own read precedes its
+    // write in program order).
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    const int nbits = 32 - __clz(nb);              // buckets 0..nb
+    for (int i0 = wb; i0 < we; i0 += kBatch * 64) {
+        if (!one_batch)
+            load_batch(i0);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c0 = i0 + u * 64;
+            if (c0 >= we)
+                break;                             // uniform
+            const int i = c0 + lane;
+            const int d = bucket(v[u]);
+            const bool valid = i < we && d < nb;
+            uint64_t same = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = (d >> b) & 1;
+                const uint64_t m = __ballot(valid && bit);
+                same &= bit ? m : ~m;
+            }
+            if (valid) {
+                const int pos = mine[d] + __popcll(same & below);
+                if ((same >> lane) == 1)           // last lane of its group
+                    mine[d] = pos + 1;
+                if (skey)                          // null when S = 1
+                    skey[beg + pos] = v[u];
+                sidx[beg + pos] = beg + i;
+            }
+        }
+    }
+}
+
+// One workgroup per bucket b (clusters b S .. b S + S - 1).  Dynamic LDS:
+// the four waves' S x D partial sums, then off[T + 1] (first slot of each
+// tile's segment) and src[T] (its first sorted position).
+template <int V, int S>
+__global__ __launch_bounds__(kBucketThreads)
+void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ skey,
+                       const int32_t *__restrict__ sidx, const int32_t *__restrict__ dir,
+                       const uint16_t *__restrict__ C_old, int D, int K, int nb, int T, int tl,
+                       uint16_t *__restrict__ C_new, float *__restrict__ means,
+                       float *__restrict__ norms, int32_t *__restrict__ counts) {
+    extern __shared__ __attribute__((aligned(16))) int bdyn[];
+    __shared__ int ck[kBucketChunk];
+    __shared__ int ci[kBucketChunk];
+    __shared__ int wtot[kBucketWaves];
+    __shared__ int bcnt[kBucketWaves][S];
+    __shared__ __attribute__((aligned(16))) uint16_t nrow[kBucketWaves][kMaxRow];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int b = blockIdx.x;
+    const bool on = lane * V < D;
+    const int col = on ? lane * V : 0;             // idle lanes load column 0
+    const int ND = nb + 1;
+    float *part = reinterpret_cast<float *>(bdyn);         // [4][S][D]
+    int *off = bdyn + kBucketWaves * S * D;                // [T + 1]
+    int *src = off + T + 1;                                // [T]
+
+    // 1. Segments: thread r owns tiles 4r .. 4r + 3 (T <= 1024); the loads
+    // are unconditional (clamped to tile T - 1) so they are in flight together.
+    constexpr int kTilesPerThread = kMaxBinTiles / kBucketThreads;
+    int seg[kTilesPerThread], sa[kTilesPerThread];
+    int sum = 0;
+    if (T > 0) {
+#pragma unroll
+        for (int u = 0; u < kTilesPerThread; ++u) {
+            const int tt = min(tid * kTilesPerThread + u, T - 1);
+            sa[u] = dir[static_cast<size_t>(tt) * ND + b];
+            seg[u] = dir[static_cast<size_t>(tt) * ND + b + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kTilesPerThread; ++u) {
+            const int tt = tid * kTilesPerThread + u;
+            seg[u] = tt < T ? seg[u] - sa[u] : 0;
+            sum += seg[u];
+        }
+    }
+    int x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        wtot[w] = x;
+    __syncthreads();
+    int ex = x - sum;
+    for (int v2 = 0; v2 < w; ++v2)
+        ex += wtot[v2];
+    const int n_pts = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+#pragma unroll
+    for (int u = 0; u < kTilesPerThread; ++u) {
+        const int tt = tid * kTilesPerThread + u;
+        if (tt < T) {
+            off[tt] = ex;
+            src[tt] = (tt << tl) + sa[u];
+            ex += seg[u];
+        }
+    }
+    if (tid == 0)
+        off[T] = n_pts;
+    __syncthreads();
+
+    // 2. Sums.  A wave takes kRows slots at a time: lane u reads slot u's
+    // point index (and cluster) from LDS, the row loads take them by
+    // readlane as scalar bases, all kRows loads in flight together.
+    constexpr int kSlotsPerThread = kBucketChunk / kBucketThreads;
+    constexpr int kRows = V == 2 ? 32 : (V == 4 ? 16 : 8);
+    float acc[S][V];
+    int cw[S];
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        cw[c] = 0;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            acc[c][v] = 0.0f;
+    }
+    for (int c0 = 0; c0 < n_pts; c0 += kBucketChunk) {
+        const int nc = min(kBucketChunk, n_pts - c0);
+        int sp[kSlotsPerThread];
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            const int slot = c0 + min(tid + u * kBucketThreads, nc - 1);
+            int lo = 0, hi = T - 1;                // last tile whose segment starts <= slot
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= slot)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            sp[u] = src[lo] + (slot - off[lo]);
+        }
+        int lk[kSlotsPerThread], li[kSlotsPerThread];
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            li[u] = sidx[sp[u]];
+            lk[u] = S > 1 ? skey[sp[u]] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            const int j = tid + u * kBucketThreads;
+            if (j < nc) {
+                ci[j] = li[u];
+                ck[j] = lk[u] & (S - 1);
+            }
+        }
+        __syncthreads();
+        const int j0 = nc * w / kBucketWaves;
+        const int j1 = nc * (w + 1) / kBucketWaves;
+        for (int jb = j0; jb < j1; jb += kRows) {
+            const int jj = min(jb + (kRows == 64 ? lane : lane % kRows), j1 - 1);
+            const int my_i = ci[jj];
+            const int my_c = S > 1 ? ck[jj] : 0;
+            RowBits<V> r[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                const int i = __builtin_amdgcn_readlane(my_i, u);
+                r[u] = load_row<V>(X + static_cast<size_t>(i) * D + col);
+            }
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                if (jb + u < j1) {                 // uniform
+                    const int c = S > 1 ? __builtin_amdgcn_readlane(my_c, u) : 0;
+#pragma unroll
+                    for (int cc = 0; cc < S; ++cc) {
+                        if (S == 1 || c == cc) {
+                            ++cw[cc];
+#pragma unroll
+                            for (int v = 0; v < V; ++v)
+                                acc[cc][v] += row_value<V>(r[u], v);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // 3. Partials of the four waves to LDS; cluster c's sum adds them in
+    // wave order.
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        if (on) {
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                part[(w * S + c) * D + lane * V + v] = acc[c][v];
+        }
+        if (lane == 0)
+            bcnt[w][c] = cw[c];
+    }
+    __syncthreads();
+
+    // 4. Outputs: wave w finishes clusters b S + w, b S + w + 4, ...
+    for (int c = w; c < S; c += kBucketWaves) {
+        const int64_t kk = static_cast<int64_t>(b) * S + c;
+        if (kk >= K)
+            break;
+        const int k = static_cast<int>(kk);
+        const int count = bcnt[0][c] + bcnt[1][c] + bcnt[2][c] + bcnt[3][c];
+        if (count == 0) {
+            uint32_t bits[V];
+            float mean[V];
+            RowBits<V> r = on ? load_row<V>(C_old + static_cast<size_t>(k) * D + lane * V)
+                              : RowBits<V>{};
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                mean[v] = row_value<V>(r, v);
+                bits[v] = __float_as_uint(mean[v]) >> 16;
+            }
+            emit_cluster<V>(k, bits, mean, 0, D, lane, nrow[w], C_new, means, norms, counts);
+        } else {
+            float s2[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                s2[v] = 0.0f;
+                if (on) {
+                    const int e = c * D + lane * V + v;
+                    s2[v] = ((part[e] + part[S * D + e]) + part[2 * S * D + e]) +
+                            part[3 * S * D + e];
+                }
+            }
+            emit_mean<V>(k, s2, count, D, lane, nrow[w], C_new, means, norms, counts);
+        }
+    }
+}
+
+template <int V, int S>
+hipError_t launch_bucket_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *skey,
+                              const int32_t *sidx, const int32_t *dir, const uint16_t *C_old,
+                              int D, int K, uint16_t *C_new, float *norms, int32_t *counts,
+                              float *means, hipStream_t stream) {
+    const size_t lds = (static_cast<size_t>(kBucketWaves) * S * D +
+                        2 * static_cast<size_t>(pl.bin_tiles) + 1) * 4;
+    hipLaunchKernelGGL((upd_bucket_kernel<V, S>), dim3(pl.buckets), dim3(kBucketThreads), lds,
+                       stream, X, skey, sidx, dir, C_old, D, K, pl.buckets, pl.bin_tiles,
+                       pl.bin_tile_log2, C_new, means, norms, counts);
+    return hipGetLastError();
+}
+
+template <int V>
+hipError_t launch_bucket_v(const UpdatePlan &pl, const uint16_t *X, const int32_t *skey,
+                           const int32_t *sidx, const int32_t *dir, const uint16_t *C_old, int D,
+                           int K, uint16_t *C_new, float *norms, int32_t *counts, float *means,
+                           hipStream_t stream) {
+    if (pl.bucket_log2 == 0)
+        return launch_bucket_sums<V, 1>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+                                        means, stream);
+    if (pl.bucket_log2 == 1)
+        return launch_bucket_sums<V, 2>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+                                        means, stream);
+    return launch_bucket_sums<V, 4>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+                                    means, stream);
+}
+
 size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 template <int V>
@@ -781,9 +1198,46 @@ hipError_t launch_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *k
 
 }  // namespace
 
-UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units) {
+// Below this many clusters there are too few buckets to fill the GPU (one
+// workgroup each), and the radix path is used.
+constexpr int64_t kMinBucketPathK = 256;
+
+bool bucket_path_fits(int64_t N, int64_t K) {
+    return N <= kMaxBinPoints && K <= kMaxBinClusters;
+}
+
+UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units, int force_path) {
     UpdatePlan p{};
     p.compute_units = compute_units > 0 ? compute_units : kDefaultComputeUnits;
+    p.path = force_path != 0 ? force_path
+                             : (K >= kMinBucketPathK && bucket_path_fits(N, K) ? 2 : 1);
+    if (p.path == 2) {
+        // Buckets of S = 2^s clusters, at most 1024 of them (one round of
+        // bucket workgroups on 256 CUs); tiles of 2^tl >= 512 points, at
+        // most 1024 of them.
+        int sl = 0;
+        while ((K + (int64_t(1) << sl) - 1) >> sl > kMaxBuckets)
+            ++sl;
+        p.bucket_log2 = sl;
+        p.buckets = static_cast<int>((K + (int64_t(1) << sl) - 1) >> sl);
+        int tl = 9;
+        while (((N + (int64_t(1) << tl) - 1) >> tl) > kMaxBinTiles)
+            ++tl;
+        p.bin_tile_log2 = tl;
+        p.bin_tiles = static_cast<int>((N + (int64_t(1) << tl) - 1) >> tl);
+        size_t off = 0;
+        if (N > 0) {
+            const size_t n4 = align_up(static_cast<size_t>(N) * 4);
+            p.sidx = off;
+            off += n4;
+            p.skey = off;
+            off += sl > 0 ? n4 : 0;
+            p.dir = off;
+            off += align_up(static_cast<size_t>(p.buckets + 1) * p.bin_tiles * 4);
+        }
+        p.bytes = off;
+        return p;
+    }
     int bits = 0;
     while ((int64_t(1) << bits) <= K)
         ++bits;                                   // keys run 0..K
@@ -831,6 +1285,28 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
                          float *norms, int32_t *counts, float *means, void *ws,
                          hipStream_t stream) {
     auto *base = static_cast<char *>(ws);
+    if (pl.path == 2) {
+        int32_t *sidx = nullptr, *skey = nullptr, *dir = nullptr;
+        if (N > 0) {
+            sidx = reinterpret_cast<int32_t *>(base + pl.sidx);
+            skey = pl.bucket_log2 > 0 ? reinterpret_cast<int32_t *>(base + pl.skey) : nullptr;
+            dir = reinterpret_cast<int32_t *>(base + pl.dir);
+            hipLaunchKernelGGL(upd_bin_kernel, dim3(pl.bin_tiles), dim3(kBinThreads), 0, stream,
+                               labels, N, K, pl.bucket_log2, pl.buckets, pl.bin_tile_log2, skey,
+                               sidx, dir);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        if (D <= 128)
+            return launch_bucket_v<2>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+                                      means, stream);
+        if (D <= 256)
+            return launch_bucket_v<4>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+                                      means, stream);
+        return launch_bucket_v<8>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+                                  means, stream);
+    }
     int32_t *start = nullptr, *end = nullptr, *keys = nullptr, *vals = nullptr;
     float *partial = nullptr;
     if (N > 0) {
@@ -894,11 +1370,13 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
 
 // ---- C entry point ---------------------------------------------------------
 
-extern "C" kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
-                                         int64_t N, int64_t D, int64_t K, void *C_new,
-                                         float *norms, int32_t *counts, float *means,
-                                         hipStream_t stream) {
+extern "C" kmeans_status_t kmeans_update_path(const void *X, const int32_t *labels,
+                                              const void *C_old, int64_t N, int64_t D, int64_t K,
+                                              void *C_new, float *norms, int32_t *counts,
+                                              float *means, int32_t path, hipStream_t stream) {
     using namespace kmeans;
+    if (path < KMEANS_UPDATE_AUTO || path > KMEANS_UPDATE_BUCKETS)
+        return fail(KMEANS_ERR_INVALID_ARG, "path=%d is not a kmeans_update_path_t", path);
     if (N < 0)
         return fail(KMEANS_ERR_INVALID_ARG, "N=%lld must be >= 0", static_cast<long long>(N));
     if (K < 1)
@@ -920,7 +1398,10 @@ extern "C" kmeans_status_t kmeans_update(const void *X, const int32_t *labels, c
         !aligned(means, 4))
         return fail(KMEANS_ERR_ALIGNMENT, "labels, norms, counts and means must be 4-byte aligned");
 
-    const UpdatePlan pl = make_update_plan(N, D, K, device_compute_units());
+    if (path == KMEANS_UPDATE_BUCKETS && !bucket_path_fits(N, K))
+        return fail(KMEANS_ERR_UNSUPPORTED, "the bucket path needs N <= 2^24 and K <= 4096 "
+                    "(N=%lld, K=%lld)", static_cast<long long>(N), static_cast<long long>(K));
+    const UpdatePlan pl = make_update_plan(N, D, K, device_compute_units(), path);
     // The stream's scratch (none when N == 0), held until the launches are queued.
     std::unique_ptr<WorkspaceLease> lease;
     void *ws = nullptr;
@@ -939,4 +1420,12 @@ extern "C" kmeans_status_t kmeans_update(const void *X, const int32_t *labels, c
     if (e != hipSuccess)
         return fail(KMEANS_ERR_HIP, "update launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+extern "C" kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
+                                         int64_t N, int64_t D, int64_t K, void *C_new,
+                                         float *norms, int32_t *counts, float *means,
+                                         hipStream_t stream) {
+    return kmeans_update_path(X, labels, C_old, N, D, K, C_new, norms, counts, means,
+                              KMEANS_UPDATE_AUTO, stream);
 }

@@ -8,6 +8,14 @@ namespace kmeans {
 
 // Workspace layout and launch shape of one kmeans_update call.
 struct UpdatePlan {
+    int path;          // 1: radix sort + chunked reduce + finish; 2: buckets
+    // path 2 (bucket_path_fits): buckets of 2^bucket_log2 clusters, sort
+    // tiles of 2^bin_tile_log2 points, workspace offsets of the sorted point
+    // indices, the sorted labels (when bucket_log2 > 0) and the
+    // [bin_tiles][buckets + 1] tile directory.
+    int bucket_log2, buckets, bin_tile_log2, bin_tiles;
+    size_t sidx, skey, dir;
+    // path 1
     int passes;        // radix passes over the keys 0..K (K = stray label)
     int digit_bits;    // bits per pass (<= 8): the key bits split evenly
     int tile_log2;     // sort tile of 2^tile_log2 points (>= 1024)
@@ -23,9 +31,14 @@ struct UpdatePlan {
     int compute_units; // reduce workgroups: four per CU
 };
 
+// Whether the bucket path supports the shape (N <= 2^24, K <= 4096).
+bool bucket_path_fits(int64_t N, int64_t K);
+
 // Requires 0 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller);
-// compute_units <= 0 means 256.
-UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units);
+// compute_units <= 0 means 256; force_path 0 (automatic), 1 or 2 (2 only
+// where bucket_path_fits).
+UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units,
+                            int force_path);
 
 // All launches of one update on `stream`; ws holds plan.bytes bytes (may be
 // null when N == 0).  means may be null.

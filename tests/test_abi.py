@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("kmeans_centroid_norms", "kmeans_assign", "kmeans_assign_static",
               "kmeans_assign_path",
-              "kmeans_plan", "kmeans_update", "kmeans_release_workspace", "kmeans_last_error",
+              "kmeans_plan", "kmeans_update", "kmeans_update_path", "kmeans_release_workspace",
+              "kmeans_last_error",
               "kmeans_abi_version"):
         assert f in names
 
@@ -242,4 +243,20 @@ def update_status(lib, X=FAKE, lab=FAKE, C=FAKE, N=10, D=64, K=5, Cn=FAKE, n=FAK
 ])
 def test_update_rejects_bad_arguments(lib, kw, status):
     assert update_status(lib, **kw) == status
+    assert lib.kmeans_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,path,status", [
+    (dict(), -1, km.KMEANS_ERR_INVALID_ARG),
+    (dict(), 3, km.KMEANS_ERR_INVALID_ARG),
+    (dict(N=(1 << 24) + 1), km.UPDATE_BUCKETS, km.KMEANS_ERR_UNSUPPORTED),
+    (dict(K=4097), km.UPDATE_BUCKETS, km.KMEANS_ERR_UNSUPPORTED),
+    (dict(X=NUL), km.UPDATE_BUCKETS, km.KMEANS_ERR_INVALID_ARG),
+])
+def test_update_path_rejects_bad_arguments(lib, kw, path, status):
+    a = dict(X=FAKE, lab=FAKE, C=FAKE, N=10, D=64, K=5, Cn=FAKE, n=FAKE, cnt=FAKE, m=NUL)
+    a.update(kw)
+    st = lib.kmeans_update_path(a["X"], a["lab"], a["C"], a["N"], a["D"], a["K"], a["Cn"],
+                                a["n"], a["cnt"], a["m"], path, NUL)
+    assert st == status
     assert lib.kmeans_last_error().decode()

@@ -42,3 +42,21 @@ def test_bench_tiny_workload_emits_the_json_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
     assert d["mfma_ceiling"]["tflops"] > 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("path", [1, 2])
+def test_bench_update_emits_the_json_line_and_checks_its_outputs(path):
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--update",
+                        "--update-path", str(path), "--config", "1", "--steps", "6",
+                        "--warmup", "2", "--settle-ms", "20", "--cpu-seconds", "0.2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["config"]["path"] == {1: "sort", 2: "buckets"}[path]
+    assert d["roofline"]["bound"] == "hbm" and d["value"] > 0
+    p = d["parity"]
+    assert p["bad_sets"] == 0 and len(p["per_seed"]) == 3
+    assert all(v["ok"] for v in p["per_seed"].values())

@@ -34,11 +34,16 @@ def host_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_update(X, lab, C, with_means=True, inplace=False):
+# Both update paths (the radix sort and the buckets) on every case that
+# fits the bucket path; the automatic choice runs in the Lloyd test.
+PATHS = pytest.mark.parametrize("path", [1, 2], ids=["sort", "buckets"])
+
+
+def run_update(X, lab, C, with_means=True, inplace=False, path=0):
     Xd, Cd = dev(X), dev(C)
     ld = torch.from_numpy(np.ascontiguousarray(lab, dtype=np.int32)).cuda()
     Cn, n, cnt, m = km.kmeans_update(Xd, ld, Cd, C_new=Cd if inplace else None,
-                                     with_means=with_means)
+                                     with_means=with_means, path=path)
     ref_norms = km.kmeans_centroid_norms(Cn)
     torch.cuda.synchronize()
     out = dict(C_new=host_bits(Cn), norms=n.cpu().numpy(), counts=cnt.cpu().numpy(),
@@ -72,15 +77,19 @@ SMALL = [  # (N, D, K): ragged everywhere, K > N, 1, 2 and 3 radix passes
 ]
 
 
+@PATHS
 @pytest.mark.parametrize("N,D,K", SMALL)
-def test_small_shapes(N, D, K):
+def test_small_shapes(N, D, K, path):
+    if path == 2 and K > 4096:
+        pytest.skip("K over the bucket path's limit (covered by the sort path)")
     X, C, a = W.gaussian_mixture(N, D, K, 300 + N + K)
     lab = noisy_labels(a, K, N)
-    st = check(X, lab, C, run_update(X, lab, C))
+    st = check(X, lab, C, run_update(X, lab, C, path=path))
     assert st["clusters"] == K
 
 
-def test_skewed_and_chunk_aligned_clusters():
+@PATHS
+def test_skewed_and_chunk_aligned_clusters(path):
     """One cluster holding most points (its rows span hundreds of reduce
     chunks), and cluster sizes that put boundaries exactly on chunk edges."""
     N, D, K = 40000, 128, 64
@@ -97,61 +106,67 @@ def test_skewed_and_chunk_aligned_clusters():
     big = np.flatnonzero(lab == 5)
     lab[rng.choice(big, 500, replace=False)] = rng.integers(10, K, 500)
     lab = lab[rng.permutation(N)]
-    out = run_update(X, lab, C)
+    out = run_update(X, lab, C, path=path)
     check(X, lab, C, out)
     assert out["counts"][8] == 0 and out["counts"][5] > 30000
 
 
-def test_all_points_one_cluster_and_all_stray():
+@PATHS
+def test_all_points_one_cluster_and_all_stray(path):
     X, C, _ = W.gaussian_mixture(9000, 64, 20, 73)
     lab = np.full(9000, 13, dtype=np.int32)
-    check(X, lab, C, run_update(X, lab, C))
+    check(X, lab, C, run_update(X, lab, C, path=path))
     lab = np.full(9000, -5, dtype=np.int32)
-    out = run_update(X, lab, C)
+    out = run_update(X, lab, C, path=path)
     check(X, lab, C, out)
     assert np.array_equal(out["C_new"], C) and not out["counts"].any()
 
 
-def test_no_points():
+@PATHS
+def test_no_points(path):
     _, C, _ = W.gaussian_mixture(1, 128, 300, 74)
     X = np.zeros((0, 128), np.uint16)
-    out = run_update(X, np.zeros(0, np.int32), C)
+    out = run_update(X, np.zeros(0, np.int32), C, path=path)
     assert np.array_equal(out["C_new"], C) and not out["counts"].any()
     assert np.array_equal(out["means"], parity._widen(C).astype(np.float32))
 
 
-def test_single_cluster():
+@PATHS
+def test_single_cluster(path):
     X, C, _ = W.gaussian_mixture(5000, 256, 1, 75)
     lab = np.zeros(5000, np.int32)
     lab[::97] = 3
-    out = run_update(X, lab, C)
+    out = run_update(X, lab, C, path=path)
     check(X, lab, C, out)
     assert out["counts"][0] == 5000 - len(lab[::97])
 
 
-def test_in_place_and_without_means_match():
+@PATHS
+def test_in_place_and_without_means_match(path):
     X, C, a = W.gaussian_mixture(6000, 128, 500, 76)
     lab = noisy_labels(a, 500, 76, relabel=0.3)
     lab[lab == 17] = 18                                  # an empty cluster
-    out = run_update(X, lab, C)
+    out = run_update(X, lab, C, path=path)
     check(X, lab, C, out)
-    out2 = run_update(X, lab, C, with_means=False, inplace=True)
+    out2 = run_update(X, lab, C, with_means=False, inplace=True, path=path)
     assert np.array_equal(out["C_new"], out2["C_new"])
     assert out["norms"].tobytes() == out2["norms"].tobytes()
     assert np.array_equal(out["counts"], out2["counts"])
 
 
-def test_repeat_calls_are_bitwise_identical():
+@PATHS
+def test_repeat_calls_are_bitwise_identical(path):
     X, C, a = W.gaussian_mixture(65536, 64, 4096, 77)
     lab = noisy_labels(a, 4096, 77)
-    outs = [run_update(X, lab, C) for _ in range(3)]
+    outs = [run_update(X, lab, C, path=path) for _ in range(3)]
     for o in outs[1:]:
         for key in ("C_new", "norms", "counts", "means"):
             assert outs[0][key].tobytes() == o[key].tobytes(), key
     check(X, lab, C, outs[0])
 
 
-def test_nonfinite_points():
+@PATHS
+def test_nonfinite_points(path):
     X, C, a = W.gaussian_mixture(3000, 64, 40, 78)
     lab = a.astype(np.int32)
     X[10, 3] = W.BF16_QNAN
@@ -161,19 +176,22 @@ def test_nonfinite_points():
     X[14, 6] = W.BF16_NINF
     lab[13] = lab[14]                                    # +inf and -inf: NaN mean
     X[15] = W.BF16_NZERO
-    out = run_update(X, lab, C)
+    out = run_update(X, lab, C, path=path)
     check(X, lab, C, out)
     m = out["means"]
     assert np.isnan(m[lab[10], 3]) and np.isnan(m[lab[13], 6])
     assert m[lab[11], 4] == np.inf and m[lab[12], 5] == -np.inf
 
 
+@PATHS
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_workload_full(cfg):
+def test_workload_full(cfg, path):
     X, C, meta = W.make_config(cfg, 17)
     K = C.shape[0]
+    if path == 2 and K > 4096:
+        pytest.skip("K over the bucket path's limit (covered by the sort path)")
     lab = noisy_labels(meta["generating_centre"], K, cfg)
-    st = check(X, lab, C, run_update(X, lab, C))
+    st = check(X, lab, C, run_update(X, lab, C, path=path))
     assert st["elements"] > 0
 
 

@@ -225,7 +225,7 @@ typedef enum {
      * scan launch when N is over 2^21), then the reduce and the finish. */
     KMEANS_UPDATE_SORT = 1,
     /* Clusters grouped into at most 1024 buckets of 1, 2 or 4 clusters;
-     * each tile of 512 or more points sorts its own points by bucket,
+     * each tile of 1024 or more points sorts its own points by bucket,
      * stably, and records where each bucket starts in it; then one
      * workgroup per bucket gathers its points tile by tile and sums their
      * rows in index order (four waves each sum a fixed quarter of every 512

@@ -777,11 +777,13 @@ void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__rest
 // all points runs on one CU (correct, but far slower than the radix path,
 // whose reduce spreads any cluster over fixed chunks).
 
-constexpr int kBinThreads = 256;     // 4 waves; each owns a quarter of the tile
-constexpr int kBinWaves = kBinThreads / 64;
+constexpr int kBinWaves = 8;         // each owns a contiguous eighth of the tile
+constexpr int kBinThreads = 64 * kBinWaves;
+constexpr int kMinBinTileLog2 = 10;
 constexpr int kMaxBuckets = 1024;
-constexpr int kBinDigitsPerThread = kMaxBuckets / kBinThreads;   // 4: one 16-byte group
-constexpr int kMaxBinTiles = 1024;
+constexpr int kScanThreads2 = 256;   // threads of the bin scan: 4 buckets each
+constexpr int kBinDigitsPerThread = kMaxBuckets / kScanThreads2;   // one 16-byte group
+constexpr int kMaxBinTiles = 512;
 constexpr int64_t kMaxBinPoints = int64_t(1) << 24;
 constexpr int kMaxBucketLog2 = 2;    // S <= 4
 constexpr int64_t kMaxBinClusters = int64_t(kMaxBuckets) << kMaxBucketLog2;
@@ -790,14 +792,14 @@ constexpr int kBucketWaves = kBucketThreads / 64;
 constexpr int kBucketChunk = 512;    // slots resolved per round
 
 // Tile t: positions [t << tl, min(N, (t + 1) << tl)).  Wave w owns the
-// contiguous quarter [w q, (w + 1) q) of the tile (q = 2^tl / 4), so the
+// contiguous eighth [w q, (w + 1) q) of the tile (q = 2^tl / 8), so the
 // stable order is: bucket, then wave, then position inside the wave.
 //  1. per-wave bucket counts (LDS atomics on the wave's own row; stray
 //     labels are not counted);
 //  2. one exclusive scan over (bucket, wave), bucket-major: cnt[w][d]
 //     becomes the first slot of (w, d), and dir[t][d] the first slot of
 //     bucket d, dir[t][nb] the number of points with a real label.  Thread
-//     r owns buckets 4r .. 4r + 3 (one 16-byte group per row);
+//     r < 256 owns buckets 4r .. 4r + 3 (one 16-byte group per row);
 //  3. each wave ranks its points 64 at a time in position order: lanes with
 //     the same bucket are found with one ballot per bucket bit, a lane's
 //     slot is the running slot of its bucket plus the earlier such lanes, and
@@ -805,7 +807,7 @@ constexpr int kBucketChunk = 512;    // slots resolved per round
 //     of every point with a real label are written at its slot.
 // Labels are loaded eight chunks (512 points) per wave at a time, all in
 // flight together (unconditional loads clamped to the wave's last point,
-// taken by an empty asm); a wave holding one batch (tiles up to 2048) keeps
+// taken by an empty asm); a wave holding one batch (tiles up to 4096) keeps
 // it in registers from the counts to the ranks.
 __global__ __launch_bounds__(kBinThreads)
 void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2, int nb,
@@ -827,8 +829,8 @@ void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2
     const int we = min(len, wb + q);
     i4 *cv = reinterpret_cast<i4 *>(cnt);
 #pragma unroll
-    for (int r = 0; r < kBinWaves; ++r)
-        cv[r * (NR / 4) + tid] = i4{0, 0, 0, 0};
+    for (int i = tid; i < kBinWaves * NR / 4; i += kBinThreads)
+        cv[i] = i4{0, 0, 0, 0};
     int v[kBatch];
     auto load_batch = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
@@ -863,18 +865,25 @@ void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2
     }
     __syncthreads();
 
-    // 2. Scan.
+    // 2. Scan: the first 256 threads own 4 buckets each (whole waves, so the
+    // shuffles below see full waves); every wave reaches both barriers.
     {
+        const bool scanner = tid < kScanThreads2;
         i4 c[kBinWaves];
-#pragma unroll
-        for (int r = 0; r < kBinWaves; ++r)
-            c[r] = cv[r * (NR / 4) + tid];
         int tot[kBinDigitsPerThread];
         int sum = 0;
+        if (scanner) {
 #pragma unroll
-        for (int j = 0; j < kBinDigitsPerThread; ++j) {
-            tot[j] = c[0][j] + c[1][j] + c[2][j] + c[3][j];
-            sum += tot[j];
+            for (int r = 0; r < kBinWaves; ++r)
+                c[r] = cv[r * (NR / 4) + tid];
+#pragma unroll
+            for (int j = 0; j < kBinDigitsPerThread; ++j) {
+                tot[j] = 0;
+#pragma unroll
+                for (int r = 0; r < kBinWaves; ++r)
+                    tot[j] += c[r][j];
+                sum += tot[j];
+            }
         }
         int x = sum;
 #pragma unroll
@@ -886,29 +895,31 @@ void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2
         if (lane == 63)
             wtot[w] = x;
         __syncthreads();
-        int ex = x - sum;
-        for (int v2 = 0; v2 < w; ++v2)
-            ex += wtot[v2];
-        int32_t *drow = dir + static_cast<size_t>(t) * (nb + 1);
-        i4 o[kBinWaves];
+        if (scanner) {
+            int ex = x - sum;
+            for (int v2 = 0; v2 < w; ++v2)
+                ex += wtot[v2];
+            int32_t *drow = dir + static_cast<size_t>(t) * (nb + 1);
+            i4 o[kBinWaves];
 #pragma unroll
-        for (int j = 0; j < kBinDigitsPerThread; ++j) {
-            const int d = tid * kBinDigitsPerThread + j;
-            if (d <= nb)
-                drow[d] = ex;
-            int run = ex;
+            for (int j = 0; j < kBinDigitsPerThread; ++j) {
+                const int d = tid * kBinDigitsPerThread + j;
+                if (d <= nb)
+                    drow[d] = ex;
+                int run = ex;
 #pragma unroll
-            for (int r = 0; r < kBinWaves; ++r) {
-                o[r][j] = run;
-                run += c[r][j];
+                for (int r = 0; r < kBinWaves; ++r) {
+                    o[r][j] = run;
+                    run += c[r][j];
+                }
+                ex += tot[j];
             }
-            ex += tot[j];
-        }
-        if (tid == kBinThreads - 1 && nb == kMaxBuckets)
-            drow[nb] = ex;                         // the total (no owner at index 1024)
+            if (tid == kScanThreads2 - 1 && nb == kMaxBuckets)
+                drow[nb] = ex;                     // the total (no owner at index 1024)
 #pragma unroll
-        for (int r = 0; r < kBinWaves; ++r)
-            cv[r * (NR / 4) + tid] = o[r];
+            for (int r = 0; r < kBinWaves; ++r)
+                cv[r * (NR / 4) + tid] = o[r];
+        }
     }
     __syncthreads();
 
@@ -947,6 +958,21 @@ void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2
     }
 }
 
+// Workgroups are dispatched to the eight XCDs in turn (workgroup i to XCD
+// i mod 8), and each XCD has its own L2.  Mapping workgroup i to item
+// start(x) + i / 8 (x = i mod 8, XCD x owning the contiguous items
+// [start(x), start(x + 1))) gives each XCD a contiguous range of buckets, so
+// the directory lines and sorted-index lines it reads are its own eighth of
+// them instead of lines shared with every other XCD.  A bijection on
+// [0, n) for any n.
+__device__ __forceinline__ int xcd_contiguous(int i, int n) {
+    constexpr int kXcds = 8;
+    const int x = i % kXcds;
+    const int q = n / kXcds;
+    const int r = n % kXcds;
+    return x * q + min(x, r) + i / kXcds;
+}
+
 // One workgroup per bucket b (clusters b S .. b S + S - 1).  Dynamic LDS:
 // the four waves' S x D partial sums, then off[T + 1] (first slot of each
 // tile's segment) and src[T] (its first sorted position).
@@ -966,7 +992,7 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
-    const int b = blockIdx.x;
+    const int b = xcd_contiguous(blockIdx.x, nb);
     const bool on = lane * V < D;
     const int col = on ? lane * V : 0;             // idle lanes load column 0
     const int ND = nb + 1;
@@ -1213,14 +1239,15 @@ UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units, 
                              : (K >= kMinBucketPathK && bucket_path_fits(N, K) ? 2 : 1);
     if (p.path == 2) {
         // Buckets of S = 2^s clusters, at most 1024 of them (one round of
-        // bucket workgroups on 256 CUs); tiles of 2^tl >= 512 points, at
-        // most 1024 of them.
+        // bucket workgroups on 256 CUs); tiles of 2^tl >= 1024 points, at
+        // most 512 of them (each bucket workgroup reads two directory
+        // entries per tile).
         int sl = 0;
         while ((K + (int64_t(1) << sl) - 1) >> sl > kMaxBuckets)
             ++sl;
         p.bucket_log2 = sl;
         p.buckets = static_cast<int>((K + (int64_t(1) << sl) - 1) >> sl);
-        int tl = 9;
+        int tl = kMinBinTileLog2;
         while (((N + (int64_t(1) << tl) - 1) >> tl) > kMaxBinTiles)
             ++tl;
         p.bin_tile_log2 = tl;

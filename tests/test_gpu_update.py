@@ -89,6 +89,18 @@ def test_small_shapes(N, D, K, path):
 
 
 @PATHS
+def test_more_than_two_million_points(path):
+    """N over 2^21: the sort path's radix passes run their scan kernel (more
+    than 128 sort tiles) and the bucket path's bin waves take their points in
+    several batches (tiles of 8192 points)."""
+    N, D, K = 3_000_000, 16, 300
+    X, C, a = W.gaussian_mixture(N, D, K, 81)
+    lab = noisy_labels(a, K, 81)
+    st = check(X, lab, C, run_update(X, lab, C, path=path))
+    assert st["clusters"] == K
+
+
+@PATHS
 def test_skewed_and_chunk_aligned_clusters(path):
     """One cluster holding most points (its rows span hundreds of reduce
     chunks), and cluster sizes that put boundaries exactly on chunk edges."""

@@ -70,10 +70,13 @@ def noisy_labels(a, K, seed, relabel=0.05, stray=0.01):
     return lab
 
 
-SMALL = [  # (N, D, K): ragged everywhere, K > N, 1, 2 and 3 radix passes
+SMALL = [  # (N, D, K): ragged everywhere, K > N, 1, 2 and 3 radix passes,
+    # buckets of 1 to 4 clusters (the last one partly past K)
     (4133, 64, 275), (1000, 16, 37), (777, 128, 300), (2050, 256, 129), (513, 512, 70),
     (300, 80, 45), (64, 32, 1), (1, 16, 5), (257, 48, 1000), (3000, 128, 2049),
     (5000, 192, 70000), (20000, 96, 255), (20000, 112, 256),
+    (9000, 64, 5000), (7000, 256, 9000), (6000, 512, 16384), (30000, 128, 12289),
+    (9000, 64, 4095), (7000, 256, 3073),
 ]
 
 

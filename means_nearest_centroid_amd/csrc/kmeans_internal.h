@@ -47,6 +47,12 @@ constexpr int assign_wgs_per_cu(int ks) {
                : (kLdsPerCu / assign_lds_bytes(ks));
 }
 constexpr int kDefaultComputeUnits = 256;   // MI355X
+// Points of one launch beyond this many bytes (the MI355X last-level cache)
+// are loaded with the non-temporal hint: they cannot stay in that cache
+// anyway, and cached they push the centroid rows out of L2, which then
+// refetches them for every round of point tiles.  Smaller launches keep
+// cached loads, so repeated calls on the same points can hit that cache.
+constexpr int64_t kStreamPointBytes = int64_t(256) << 20;
 
 // MFMA geometry of the assign kernel for a padded width of 16*ks: 16 =
 // v_mfma_f32_16x16x32_bf16, 32 = v_mfma_f32_32x32x16_bf16.  Back to back on

@@ -222,6 +222,11 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// The same with the non-temporal hint (cache policy NT on gfx950).
+__device__ __forceinline__ u32x4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 // An offset past every buffer's num_records: point tiles span at most 512
 // KiB and a K-range at most kMaxRangeBytes (< 2^31) of centroid rows.
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -415,7 +420,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
                    const float *__restrict__ norms, int N, int D, int K, int k_chunk,
-                   int write_partials, int32_t *__restrict__ labels,
+                   int write_partials, int x_stream, int32_t *__restrict__ labels,
                    float *__restrict__ min_dist, float *__restrict__ ws_score,
                    int32_t *__restrict__ ws_label, float *__restrict__ ws_xx) {
     // MFMA geometry.  G = 32: v_mfma_f32_32x32x16_bf16, one 32-row A block
@@ -725,15 +730,25 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     // which waits for the points, does not hold the DMA back.
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + static_cast<size_t>(wg_point0) * D,
                                                 static_cast<uint32_t>(wg_points) * row_bytes);
+    // x_stream (wave-uniform): the launch's points are larger than the
+    // last-level cache, so they are loaded with the non-temporal hint and do
+    // not push the centroid rows out of L2.
+    auto load_points = [&](auto nt) KM_INLINE {
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-        const uint32_t prow = static_cast<uint32_t>(wave * P * kTileCols + p * G + pcol);
+        for (int p = 0; p < PB; ++p) {
+            const uint32_t prow = static_cast<uint32_t>(wave * P * kTileCols + p * G + pcol);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int c0 = ks * KSTEP + kq * 8;
-            xb[p][ks] = load16(xr, c0 < D ? prow * row_bytes + c0 * 2 : kOutOfRange);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int c0 = ks * KSTEP + kq * 8;
+                const uint32_t off = c0 < D ? prow * row_bytes + c0 * 2 : kOutOfRange;
+                xb[p][ks] = decltype(nt)::value ? load16_nt(xr, off) : load16(xr, off);
+            }
         }
-    }
+    };
+    if (x_stream)
+        load_points(std::true_type{});
+    else
+        load_points(std::false_type{});
     // Keep the conversion below the loads: pulled up between them, each of its
     // waits would also wait for block 0's DMA (loads complete in order).
     __builtin_amdgcn_sched_barrier(0);
@@ -962,9 +977,10 @@ hipError_t launch_assign_kp(const Plan &pl, const uint16_t *X, const uint16_t *C
     constexpr int WPE = waves_per_simd(KS);
     static_assert(assign_wgs_per_cu(KS) >= 1, "workgroup must fit a CU");
     const int partial = ws_score != nullptr ? 1 : 0;
+    const int x_stream = static_cast<int64_t>(N) * D * 2 > kStreamPointBytes ? 1 : 0;
     hipLaunchKernelGGL((assign_kernel<mfma_geometry(KS), KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
-                       0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, labels, min_dist,
-                       ws_score, ws_label, ws_xx);
+                       0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, x_stream, labels,
+                       min_dist, ws_score, ws_label, ws_xx);
     return hipGetLastError();
 }
 

@@ -32,13 +32,23 @@
 //    reduced to its minimum with v_min3 (half an op per score) and the exact
 //    slot is searched only when that minimum beats the running best: about
 //    ln(K) times per point over a scan, though a wave (64 lanes) still takes
-//    that branch on most tiles early in K and fewer later.  Ties keep the
-//    lower index at every level; the two lanes that share a point merge by
-//    (score, index) ("Deterministic winner merge").  The N x K score matrix
-//    never leaves registers.
-//  * A point whose every score is +inf or NaN, or whose result is not finite,
-//    takes a cold per-lane path after the loop (rule: -inf < finite < +inf <
-//    NaN, ties to the lower index).
+//    that branch on most tiles early in K and fewer later.  The lanes that
+//    share a point (four, or two with 32x32x16) exchange their bests every
+//    few tiles and compare against the point's best, which halves the
+//    searches; where the registers allow (one point block per wave, or a
+//    whole SIMD at D = 512) an improving lane only copies the tile's scores
+//    and searches them once after the loop.  Ties keep the lower index at
+//    every level; the lanes of a point merge by (score, index)
+//    ("Deterministic winner merge").  The N x K score matrix never leaves
+//    registers.
+//  * min_dist is ||x||^2 + s for the winner while that expansion is
+//    accurate for the wave's points, else the direct sum of (x - c)^2 over
+//    the winner's row.
+//  * A launch whose points exceed the last-level cache streams them past L2
+//    (non-temporal loads), so they do not evict the centroid rows.
+//  * A point whose every score is +inf or NaN takes a cold per-lane path
+//    after the loop (rule: -inf < finite < +inf < NaN, ties to the lower
+//    index).
 #include <math.h>
 #include <stdint.h>
 

@@ -60,14 +60,24 @@ constexpr int64_t kStreamPointBytes = int64_t(256) << 20;
 // (it reads half the accumulator registers per flop), and its half-size
 // accumulators leave room for reduction rotation at D >= 256; at D <= 64 a
 // 16x16x32 point block holds only two k-steps, too little matrix time to
-// hide its reduction behind, so the 32x32x16 form stays there; at D = 512
+// hide its reduction behind when a few waves run alone, so the 32x32x16 form
+// is the default there (large calls at D = 64 switch, below); at D = 512
 // two 16x16x32 point blocks of 16 k-steps spill, and one 32x32x16 block
-// does not.  Every path of one D uses the same form, so their outputs stay
-// bitwise identical.
+// does not.  Every launch of one call uses the same form (Plan::geom), so
+// the paths' outputs stay bitwise identical.
 constexpr int mfma_geometry(int ks) { return ks == 8 || ks == 16 ? 16 : 32; }
+// At D = 64 (ks = 4) a call with at least this much work (N K) takes the
+// 16x16x32 form after all: with many workgroups per CU its two k-steps per
+// B block are hidden by the other waves, and its fragments are read once per
+// two B blocks (measured 1.5-6% faster from 65536 x 4096 up); smaller calls,
+// where a few waves run alone, keep 32x32x16 (3-16% faster there).  The form
+// is chosen per call, so all launches of a call (split ranges, the narrow
+// tail) use the same one and agree bitwise.
+constexpr int64_t kG16MinWorkAtD64 = int64_t(1) << 28;
 
 struct Plan {
     int path;          // 1 direct, 2 split (as kmeans_path_t)
+    int geom;          // MFMA form: 16 (16x16x32) or 32 (32x32x16)
     int splits;        // K-ranges (grid.y)
     int ks;            // padded D / 16
     int pb;            // point blocks per wave (wide_point_blocks(ks) or 1)

@@ -918,14 +918,13 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 // uses for the geometry G of this D (lane q of a point adds its 8-wide
 // chunks q*8, q*8 + KSTEP, ...; the lanes' sums combine pairwise), so split
 // and direct outputs are bitwise equal.
-template <int KS>
+template <int KS, int G>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void merge_kernel(const float *__restrict__ ws_score, const int32_t *__restrict__ ws_label,
                   const float *__restrict__ ws_xx, int splits,
                   const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
                   const float *__restrict__ norms, int N, int D, int K,
                   int32_t *__restrict__ labels, float *__restrict__ min_dist) {
-    constexpr int G = mfma_geometry(KS);
     constexpr int KSTEP = G == 32 ? 16 : 32;
     constexpr int LANES = 64 / G;
     const int n = blockIdx.x * kThreads + threadIdx.x;
@@ -977,7 +976,7 @@ void norms_kernel(const uint16_t *__restrict__ C, int K, int D, float *__restric
         norms[row] = n;
 }
 
-template <int KS, int P>
+template <int KS, int G, int P>
 hipError_t launch_assign_kp(const Plan &pl, const uint16_t *X, const uint16_t *C,
                             const float *norms, int N, int D, int K, int32_t *labels,
                             float *min_dist, float *ws_score, int32_t *ws_label,
@@ -988,10 +987,23 @@ hipError_t launch_assign_kp(const Plan &pl, const uint16_t *X, const uint16_t *C
     static_assert(assign_wgs_per_cu(KS) >= 1, "workgroup must fit a CU");
     const int partial = ws_score != nullptr ? 1 : 0;
     const int x_stream = static_cast<int64_t>(N) * D * 2 > kStreamPointBytes ? 1 : 0;
-    hipLaunchKernelGGL((assign_kernel<mfma_geometry(KS), KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
+    hipLaunchKernelGGL((assign_kernel<G, KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
                        0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, x_stream, labels,
                        min_dist, ws_score, ws_label, ws_xx);
     return hipGetLastError();
+}
+
+template <int KS, int G>
+hipError_t launch_assign_kg(const Plan &pl, const uint16_t *X, const uint16_t *C,
+                            const float *norms, int N, int D, int K, int32_t *labels,
+                            float *min_dist, float *ws_score, int32_t *ws_label,
+                            float *ws_xx, hipStream_t stream) {
+    constexpr int WIDE = wide_point_blocks(KS);
+    if (WIDE > 1 && pl.pb == 1)
+        return launch_assign_kp<KS, G, 1>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
+                                          ws_label, ws_xx, stream);
+    return launch_assign_kp<KS, G, WIDE>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
+                                         ws_label, ws_xx, stream);
 }
 
 template <int KS>
@@ -999,12 +1011,13 @@ hipError_t launch_assign_ks(const Plan &pl, const uint16_t *X, const uint16_t *C
                             const float *norms, int N, int D, int K, int32_t *labels,
                             float *min_dist, float *ws_score, int32_t *ws_label,
                             float *ws_xx, hipStream_t stream) {
-    constexpr int WIDE = wide_point_blocks(KS);
-    if (WIDE > 1 && pl.pb == 1)
-        return launch_assign_kp<KS, 1>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
-                                       ws_label, ws_xx, stream);
-    return launch_assign_kp<KS, WIDE>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
-                                      ws_label, ws_xx, stream);
+    if constexpr (KS == 4) {
+        if (pl.geom == 16)
+            return launch_assign_kg<KS, 16>(pl, X, C, norms, N, D, K, labels, min_dist,
+                                            ws_score, ws_label, ws_xx, stream);
+    }
+    return launch_assign_kg<KS, mfma_geometry(KS)>(pl, X, C, norms, N, D, K, labels, min_dist,
+                                                   ws_score, ws_label, ws_xx, stream);
 }
 
 }  // namespace
@@ -1035,16 +1048,22 @@ hipError_t launch_merge(const Plan &pl, const uint16_t *X, const uint16_t *C,
                         float *min_dist, const float *ws_score, const int32_t *ws_label,
                         const float *ws_xx, hipStream_t stream) {
     const int blocks = (N + kThreads - 1) / kThreads;
-#define KM_MERGE(KSV)                                                                       \
-    hipLaunchKernelGGL(merge_kernel<KSV>, dim3(blocks), dim3(kThreads), 0, stream, ws_score, \
-                       ws_label, ws_xx, pl.splits, X, C, norms, N, D, K, labels, min_dist)
+#define KM_MERGE(KSV, GV)                                                                   \
+    hipLaunchKernelGGL((merge_kernel<KSV, GV>), dim3(blocks), dim3(kThreads), 0, stream,     \
+                       ws_score, ws_label, ws_xx, pl.splits, X, C, norms, N, D, K, labels,    \
+                       min_dist)
     switch (pl.ks) {
-    case 1: KM_MERGE(1); break;
-    case 2: KM_MERGE(2); break;
-    case 4: KM_MERGE(4); break;
-    case 8: KM_MERGE(8); break;
-    case 16: KM_MERGE(16); break;
-    case 32: KM_MERGE(32); break;
+    case 1: KM_MERGE(1, mfma_geometry(1)); break;
+    case 2: KM_MERGE(2, mfma_geometry(2)); break;
+    case 4:
+        if (pl.geom == 16)
+            KM_MERGE(4, 16);
+        else
+            KM_MERGE(4, mfma_geometry(4));
+        break;
+    case 8: KM_MERGE(8, mfma_geometry(8)); break;
+    case 16: KM_MERGE(16, mfma_geometry(16)); break;
+    case 32: KM_MERGE(32, mfma_geometry(32)); break;
     default: return hipErrorInvalidValue;
     }
 #undef KM_MERGE
@@ -1070,6 +1089,7 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
     while (ks < ks_needed)
         ks <<= 1;
     pl.ks = ks;
+    pl.geom = ks == 4 && N * K >= kG16MinWorkAtD64 ? 16 : mfma_geometry(ks);
     pl.bk = k_block_rows(ks);
     const int nkb = static_cast<int>((K + pl.bk - 1) / pl.bk);   // centroid blocks
     const int cus = compute_units > 0 ? compute_units : kDefaultComputeUnits;

@@ -528,7 +528,34 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
         for (int ks = 0; ks < NKS; ++ks)
             a_off[m][ks] = row * ROW_BYTES + swz<S>(row, ks * (KSTEP / 8) + kq) * 16;
     }
+    // Where two stages span more than 64 KiB of LDS, stage 1's reads lie
+    // beyond a ds_read's 16-bit offset, so its per-lane offsets are kept with
+    // the stage's address added (opaque to the compiler, which would
+    // otherwise fold the stage address into each read's constant and add it
+    // on the VALU; the low 32 bits of a flat LDS address are its LDS
+    // offset): every fragment read is then one base register plus the tile's
+    // row offset as the immediate.  Smaller stages need no such
+    // registers; at D = 512 the 32 registers they take cost more than the
+    // adds they save (3% slower at 262144 x 512 x 4096; +0.9% at D = 128).
+    constexpr bool ST1_BASE = 2 * STAGE_BYTES > 65536 && MB * NKS <= 8;
+    uint32_t a_off1[ST1_BASE ? MB : 1][ST1_BASE ? NKS : 1];
+#pragma unroll
+    for (int m = 0; m < (ST1_BASE ? MB : 0); ++m)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            a_off1[m][ks] = static_cast<uint32_t>(a_off[m][ks]) +
+                            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                                static_cast<const uint8_t *>(c_st1)));
+            asm volatile("" : "+v"(a_off1[m][ks]));
+        }
     auto read_a = [&](const uint8_t *stage, int r0, int m, int ks) KM_INLINE {
+        if constexpr (ST1_BASE) {
+            if (stage == c_st1) {
+                const uint32_t addr = a_off1[m][ks] + static_cast<uint32_t>(r0 * ROW_BYTES);
+                return __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<KM_LDS const u32x4 *>(static_cast<uintptr_t>(addr)));
+            }
+        }
         return __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4 *>(&stage[r0 * ROW_BYTES + a_off[m][ks]]));
     };

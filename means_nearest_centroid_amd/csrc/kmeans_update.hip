@@ -790,6 +790,8 @@ constexpr int64_t kMaxBinClusters = int64_t(kMaxBuckets) << kMaxBucketLog2;
 constexpr int kBucketThreads = 256;  // 4 waves
 constexpr int kBucketWaves = kBucketThreads / 64;
 constexpr int kBucketChunk = 512;    // slots resolved per round
+constexpr int kSlotIdxBits = 24;     // a slot word: point index | cluster in bucket << 24
+static_assert(kMaxBinPoints <= (int64_t(1) << kSlotIdxBits), "point indices fit the slot word");
 
 // Tile t: positions [t << tl, min(N, (t + 1) << tl)).  Wave w owns the
 // contiguous eighth [w q, (w + 1) q) of the tile (q = 2^tl / 8), so the
@@ -803,16 +805,16 @@ constexpr int kBucketChunk = 512;    // slots resolved per round
 //  3. each wave ranks its points 64 at a time in position order: lanes with
 //     the same bucket are found with one ballot per bucket bit, a lane's
 //     slot is the running slot of its bucket plus the earlier such lanes, and
-//     the group's last lane advances the running slot.  The label and index
-//     of every point with a real label are written at its slot.
+//     the group's last lane advances the running slot.  Every point with a
+//     real label writes one word at its slot: its index (below 2^24) in the
+//     low 24 bits, its cluster within the bucket (label mod S) above them.
 // Labels are loaded eight chunks (512 points) per wave at a time, all in
 // flight together (unconditional loads clamped to the wave's last point,
 // taken by an empty asm); a wave holding one batch (tiles up to 4096) keeps
 // it in registers from the counts to the ranks.
 __global__ __launch_bounds__(kBinThreads)
 void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2, int nb,
-                    int tl, int32_t *__restrict__ skey, int32_t *__restrict__ sidx,
-                    int32_t *__restrict__ dir) {
+                    int tl, int32_t *__restrict__ sidx, int32_t *__restrict__ dir) {
     typedef int32_t i4 __attribute__((ext_vector_type(4)));
     __shared__ __attribute__((aligned(16))) int cnt[kBinWaves * kMaxBuckets];
     __shared__ int wtot[kBinWaves];
@@ -950,9 +952,7 @@ void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2
                 const int pos = mine[d] + __popcll(same & below);
                 if ((same >> lane) == 1)           // last lane of its group
                     mine[d] = pos + 1;
-                if (skey)                          // null when S = 1
-                    skey[beg + pos] = v[u];
-                sidx[beg + pos] = beg + i;
+                sidx[beg + pos] = (beg + i) | ((v[u] & ((1 << s_log2) - 1)) << kSlotIdxBits);
             }
         }
     }
@@ -978,13 +978,12 @@ __device__ __forceinline__ int xcd_contiguous(int i, int n) {
 // tile's segment) and src[T] (its first sorted position).
 template <int V, int S>
 __global__ __launch_bounds__(kBucketThreads)
-void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ skey,
-                       const int32_t *__restrict__ sidx, const int32_t *__restrict__ dir,
+void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ sidx,
+                       const int32_t *__restrict__ dir,
                        const uint16_t *__restrict__ C_old, int D, int K, int nb, int T, int tl,
                        uint16_t *__restrict__ C_new, float *__restrict__ means,
                        float *__restrict__ norms, int32_t *__restrict__ counts) {
     extern __shared__ __attribute__((aligned(16))) int bdyn[];
-    __shared__ int ck[kBucketChunk];
     __shared__ int ci[kBucketChunk];
     __shared__ int wtot[kBucketWaves];
     __shared__ int bcnt[kBucketWaves][S];
@@ -1000,8 +999,11 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
     int *off = bdyn + kBucketWaves * S * D;                // [T + 1]
     int *src = off + T + 1;                                // [T]
 
-    // 1. Segments: thread r owns tiles 4r .. 4r + 3 (T <= 1024); the loads
-    // are unconditional (clamped to tile T - 1) so they are in flight together.
+    // 1. Segments: thread r owns tiles 2r, 2r + 1 (T <= 512); the loads are
+    // unconditional (clamped to tile T - 1) so they are in flight together,
+    // and each takes a tile's two adjacent entries at once (8 bytes, 4-byte
+    // aligned, which global loads allow).
+    typedef int32_t i2 __attribute__((ext_vector_type(2)));
     constexpr int kTilesPerThread = kMaxBinTiles / kBucketThreads;
     int seg[kTilesPerThread], sa[kTilesPerThread];
     int sum = 0;
@@ -1009,8 +1011,10 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
 #pragma unroll
         for (int u = 0; u < kTilesPerThread; ++u) {
             const int tt = min(tid * kTilesPerThread + u, T - 1);
-            sa[u] = dir[static_cast<size_t>(tt) * ND + b];
-            seg[u] = dir[static_cast<size_t>(tt) * ND + b + 1];
+            i2 pr;
+            __builtin_memcpy(&pr, dir + static_cast<size_t>(tt) * ND + b, sizeof(pr));
+            sa[u] = pr.x;
+            seg[u] = pr.y;
         }
 #pragma unroll
         for (int u = 0; u < kTilesPerThread; ++u) {
@@ -1076,27 +1080,24 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
             }
             sp[u] = src[lo] + (slot - off[lo]);
         }
-        int lk[kSlotsPerThread], li[kSlotsPerThread];
+        int li[kSlotsPerThread];
 #pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
+        for (int u = 0; u < kSlotsPerThread; ++u)
             li[u] = sidx[sp[u]];
-            lk[u] = S > 1 ? skey[sp[u]] : 0;
-        }
 #pragma unroll
         for (int u = 0; u < kSlotsPerThread; ++u) {
             const int j = tid + u * kBucketThreads;
-            if (j < nc) {
+            if (j < nc)
                 ci[j] = li[u];
-                ck[j] = lk[u] & (S - 1);
-            }
         }
         __syncthreads();
         const int j0 = nc * w / kBucketWaves;
         const int j1 = nc * (w + 1) / kBucketWaves;
         for (int jb = j0; jb < j1; jb += kRows) {
             const int jj = min(jb + (kRows == 64 ? lane : lane % kRows), j1 - 1);
-            const int my_i = ci[jj];
-            const int my_c = S > 1 ? ck[jj] : 0;
+            const int word = ci[jj];
+            const int my_i = word & ((1 << kSlotIdxBits) - 1);
+            const int my_c = S > 1 ? word >> kSlotIdxBits : 0;
             RowBits<V> r[kRows];
 #pragma unroll
             for (int u = 0; u < kRows; ++u) {
@@ -1171,30 +1172,30 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
 }
 
 template <int V, int S>
-hipError_t launch_bucket_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *skey,
-                              const int32_t *sidx, const int32_t *dir, const uint16_t *C_old,
-                              int D, int K, uint16_t *C_new, float *norms, int32_t *counts,
-                              float *means, hipStream_t stream) {
+hipError_t launch_bucket_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *sidx,
+                              const int32_t *dir, const uint16_t *C_old, int D, int K,
+                              uint16_t *C_new, float *norms, int32_t *counts, float *means,
+                              hipStream_t stream) {
     const size_t lds = (static_cast<size_t>(kBucketWaves) * S * D +
                         2 * static_cast<size_t>(pl.bin_tiles) + 1) * 4;
     hipLaunchKernelGGL((upd_bucket_kernel<V, S>), dim3(pl.buckets), dim3(kBucketThreads), lds,
-                       stream, X, skey, sidx, dir, C_old, D, K, pl.buckets, pl.bin_tiles,
+                       stream, X, sidx, dir, C_old, D, K, pl.buckets, pl.bin_tiles,
                        pl.bin_tile_log2, C_new, means, norms, counts);
     return hipGetLastError();
 }
 
 template <int V>
-hipError_t launch_bucket_v(const UpdatePlan &pl, const uint16_t *X, const int32_t *skey,
-                           const int32_t *sidx, const int32_t *dir, const uint16_t *C_old, int D,
-                           int K, uint16_t *C_new, float *norms, int32_t *counts, float *means,
+hipError_t launch_bucket_v(const UpdatePlan &pl, const uint16_t *X, const int32_t *sidx,
+                           const int32_t *dir, const uint16_t *C_old, int D, int K,
+                           uint16_t *C_new, float *norms, int32_t *counts, float *means,
                            hipStream_t stream) {
     if (pl.bucket_log2 == 0)
-        return launch_bucket_sums<V, 1>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+        return launch_bucket_sums<V, 1>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
                                         means, stream);
     if (pl.bucket_log2 == 1)
-        return launch_bucket_sums<V, 2>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+        return launch_bucket_sums<V, 2>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
                                         means, stream);
-    return launch_bucket_sums<V, 4>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+    return launch_bucket_sums<V, 4>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
                                     means, stream);
 }
 
@@ -1257,8 +1258,6 @@ UpdatePlan make_update_plan(int64_t N, int64_t D, int64_t K, int compute_units, 
             const size_t n4 = align_up(static_cast<size_t>(N) * 4);
             p.sidx = off;
             off += n4;
-            p.skey = off;
-            off += sl > 0 ? n4 : 0;
             p.dir = off;
             off += align_up(static_cast<size_t>(p.buckets + 1) * p.bin_tiles * 4);
         }
@@ -1313,25 +1312,24 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
                          hipStream_t stream) {
     auto *base = static_cast<char *>(ws);
     if (pl.path == 2) {
-        int32_t *sidx = nullptr, *skey = nullptr, *dir = nullptr;
+        int32_t *sidx = nullptr, *dir = nullptr;
         if (N > 0) {
             sidx = reinterpret_cast<int32_t *>(base + pl.sidx);
-            skey = pl.bucket_log2 > 0 ? reinterpret_cast<int32_t *>(base + pl.skey) : nullptr;
             dir = reinterpret_cast<int32_t *>(base + pl.dir);
             hipLaunchKernelGGL(upd_bin_kernel, dim3(pl.bin_tiles), dim3(kBinThreads), 0, stream,
-                               labels, N, K, pl.bucket_log2, pl.buckets, pl.bin_tile_log2, skey,
-                               sidx, dir);
+                               labels, N, K, pl.bucket_log2, pl.buckets, pl.bin_tile_log2, sidx,
+                               dir);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
         }
         if (D <= 128)
-            return launch_bucket_v<2>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+            return launch_bucket_v<2>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
                                       means, stream);
         if (D <= 256)
-            return launch_bucket_v<4>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+            return launch_bucket_v<4>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
                                       means, stream);
-        return launch_bucket_v<8>(pl, X, skey, sidx, dir, C_old, D, K, C_new, norms, counts,
+        return launch_bucket_v<8>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
                                   means, stream);
     }
     int32_t *start = nullptr, *end = nullptr, *keys = nullptr, *vals = nullptr;

@@ -10,11 +10,11 @@ namespace kmeans {
 struct UpdatePlan {
     int path;          // 1: radix sort + chunked reduce + finish; 2: buckets
     // path 2 (bucket_path_fits): buckets of 2^bucket_log2 clusters, sort
-    // tiles of 2^bin_tile_log2 points, workspace offsets of the sorted point
-    // indices, the sorted labels (when bucket_log2 > 0) and the
-    // [bin_tiles][buckets + 1] tile directory.
+    // tiles of 2^bin_tile_log2 points, workspace offsets of the sorted slot
+    // words (point index, cluster in bucket) and the [bin_tiles][buckets + 1]
+    // tile directory.
     int bucket_log2, buckets, bin_tile_log2, bin_tiles;
-    size_t sidx, skey, dir;
+    size_t sidx, dir;
     // path 1
     int passes;        // radix passes over the keys 0..K (K = stray label)
     int digit_bits;    // bits per pass (<= 8): the key bits split evenly

@@ -5,6 +5,8 @@ relabelled at random and some stray labels outside [0, K) -- never labels
 computed by the HIP path.  Acceptance rule: ``parity.check_update``.
 """
 
+import functools
+
 import numpy as np
 import pytest
 
@@ -99,6 +101,24 @@ def test_more_than_two_million_points(path):
     N, D, K = 3_000_000, 16, 300
     X, C, a = W.gaussian_mixture(N, D, K, 81)
     lab = noisy_labels(a, K, 81)
+    st = check(X, lab, C, run_update(X, lab, C, path=path))
+    assert st["clusters"] == K
+
+
+@functools.lru_cache(maxsize=1)
+def _largest_bucket_path_set():
+    N, D, K = 1 << 24, 16, 4096
+    X, C, a = W.gaussian_mixture(N, D, K, 83)
+    return X, C, noisy_labels(a, K, 83)
+
+
+@PATHS
+def test_largest_bucket_path_shape(path):
+    """N = 2^24, the bucket path's limit, with buckets of four clusters: the
+    last point indices fill all 24 index bits of a sorted slot word next to
+    its two cluster bits, and the bin tiles hold 32768 points each."""
+    X, C, lab = _largest_bucket_path_set()
+    K = C.shape[0]
     st = check(X, lab, C, run_update(X, lab, C, path=path))
     assert st["clusters"] == K
 

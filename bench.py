@@ -165,8 +165,10 @@ PAGES_B200_PR_MS = {
 def run_sweep(args):
     """The pages' 13-shape benchmark: per shape, three seeded sets resident
     and rotated, ``args.settle_ms`` of untimed calls, ``args.warmup``
-    untimed then ``args.steps`` timed ``kmeans_assign`` calls (HIP events on
-    the launch stream), median latency; one JSON line per shape, then a
+    untimed calls, then three rounds of ``args.steps`` back-to-back
+    ``kmeans_assign`` calls, each round bracketed by HIP events on the launch
+    stream (no event between calls: one costs 3-4 us of stream time); the
+    median of the rounds' per-call times; one JSON line per shape, then a
     geometric-mean line."""
     import torch
     import means_nearest_centroid_amd as km
@@ -196,17 +198,18 @@ def run_sweep(args):
         for i in range(args.warmup):
             call(i)
         torch.cuda.synchronize()
-        ts = []
-        for i in range(args.steps):
-            X, C, n = sets[i % 3]
+        rounds = []
+        for _ in range(3):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
             e0.record(stream)
-            km.kmeans_assign(X, C, n, labels, min_dist, stream=stream)
+            for i in range(args.steps):
+                call(i)
             e1.record(stream)
-            ts.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = np.array([a.elapsed_time(b) for a, b in ts])
+            torch.cuda.synchronize()
+            rounds.append(e0.elapsed_time(e1) / args.steps)
+        ms = np.array(rounds)
         med = float(np.median(ms))
         plan = km.kmeans_plan(N, D, K, cus)
         tflops = 2.0 * N * D * K / (med / 1e3) / 1e12
@@ -217,8 +220,7 @@ def run_sweep(args):
             "sweep_shape": {"N": N, "D": D, "K": K},
             "path": "split" if plan["path"] == km.PATH_SPLIT else "direct",
             "splits": plan["splits"],
-            "median_ms": round(med, 4), "min_ms": round(float(ms.min()), 4),
-            "p90_ms": round(float(np.percentile(ms, 90)), 4),
+            "ms": round(med, 4), "rounds_ms": [round(float(v), 4) for v in ms],
             "points_per_s": N / (med / 1e3),
             "tflops": round(tflops, 1),
             "frac_bf16_peak": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
@@ -448,33 +450,30 @@ def run_update(args):
              torch.empty(K, dtype=torch.int32, device=dev)) for _ in sets]
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         X, lab, C = sets[i % len(sets)]
         C_new, norms, counts = outs[i % len(sets)]
         km.kmeans_update(X, lab, C, C_new, norms, counts, stream=stream, path=args.update_path)
-        if ev is not None:
-            ev.record(stream)
 
     settled = settle(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # One event after each call: calls run back to back, so call i's time
-    # is the span from the previous call's event (or the start) to its own.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: K calls back to back, bracketed by synchronisation and
+    # by GPU events on the launch stream, nothing else enqueued between the
+    # calls (a timing event between two launches costs 3-4 us of stream time
+    # here); a call's time is the region's over K.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     end.record(stream)
     enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-    call_ms = np.array([(start if i == 0 else evs[i - 1]).elapsed_time(evs[i])
-                        for i in range(args.steps)])
     print(f"[bench] update: {ms_per_step * 1e3:.1f} us per call on the GPU, "
           f"{enqueue / args.steps * 1e6:.1f} us per call to enqueue on the host",
           file=sys.stderr, flush=True)
@@ -490,7 +489,7 @@ def run_update(args):
     timed = [(o[0].view(torch.int16).cpu().numpy().view(np.uint16), o[1].cpu().numpy(),
               o[2].cpu().numpy()) for o in outs]
     nbytes = update_bytes(N, D, K)
-    avg_s = float(call_ms.mean()) / 1e3
+    avg_s = ms_per_step / 1e3
     achieved = nbytes / avg_s / 1e9
     traffic = traffic_record(args.config, "update")
     cpu = None
@@ -552,9 +551,6 @@ def run_update(args):
                          avg_launch_us=round(avg_s * 1e6, 2), bytes_per_launch=nbytes),
         "cpu_baseline": cpu,
         "parity": timed_parity,
-        "breakdown_us": {"call_median": round(float(np.median(call_ms)) * 1e3, 2),
-                         "call_min": round(float(call_ms.min()) * 1e3, 2),
-                         "call_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
     }
     print(json.dumps(out), flush=True)
     if bad_sets:
@@ -636,16 +632,33 @@ def main():
     stream = torch.cuda.current_stream()
     plan = km.kmeans_plan(N, D, K, torch.cuda.get_device_properties(dev).multi_processor_count)
 
-    def step(i, ev=None):
+    def norms_only(i):
+        j = i % len(sets)
+        km.kmeans_centroid_norms(sets[j][1], norms[j], stream=stream)
+
+    def assign_only(i):
         j = i % len(sets)
         X, C = sets[j]
-        n = norms[j]
-        km.kmeans_centroid_norms(C, n, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        km.kmeans_assign(X, C, n, labels[j], min_dist[j], stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        km.kmeans_assign(X, C, norms[j], labels[j], min_dist[j], stream=stream)
+
+    def step(i):
+        norms_only(i)
+        assign_only(i)
+
+    def region_ms(fn):
+        # Per-call time of args.steps calls back to back, bracketed by
+        # synchronisation and by GPU events on the launch stream, nothing
+        # else enqueued between the calls (a timing event between two
+        # launches costs 3-4 us of stream time here).
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
 
     settled = settle(step, args.settle_ms)
     print(f"[bench] settled clocks with {settled} untimed steps; warmup {args.warmup} steps",
@@ -654,31 +667,25 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K steps bracketed by synchronisation, GPU events on the
-    # launch stream around the whole region and around each assign launch;
-    # a step's norms launch runs alone between the previous step's last
-    # event (or the start) and its own first one, so two events per step
-    # time both kernels.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # Timed region: K steps (norms + assign) back to back, bracketed by
+    # synchronisation and by GPU events on the launch stream.
     t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = region_ms(step)
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    norms_ms = np.array([(start if i == 0 else evs[i - 1][1]).elapsed_time(evs[i][0])
-                         for i in range(args.steps)])
-    assign_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    total_ms = ms_per_step * args.steps
     print(f"[bench] {args.steps} steps: {total_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall",
           file=sys.stderr, flush=True)
-    # Outputs of the timed calls, before any later step overwrites them.
+    # Outputs of the timed calls, before any later launch overwrites them.
     timed_outputs = [(lab.cpu().numpy(), md.cpu().numpy()) for lab, md in zip(labels, min_dist)]
+    # Each kernel's average launch time, right after the timed steps: K
+    # back-to-back launches of it alone on the same rotating sets, timed the
+    # same way (every set's norms written first).
+    for j in range(len(sets)):
+        norms_only(j)
+    assign_ms = region_ms(assign_only)
+    norms_ms = region_ms(norms_only)
+    print(f"[bench] per launch: assign {assign_ms * 1e3:.2f} us, norms {norms_ms * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
 
     if args.copy_calibration_mib:
         # A plain streaming kernel of known traffic (read n bytes, write n
@@ -693,7 +700,7 @@ def main():
               file=sys.stderr, flush=True)
 
     flops = 2.0 * N * D * K
-    avg_assign_s = float(assign_ms.mean()) / 1e3
+    avg_assign_s = assign_ms / 1e3
     achieved = flops / avg_assign_s / 1e12
     traffic = traffic_record(args.config)
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_DENSE_PEAK_TFLOPS,
@@ -761,13 +768,11 @@ def main():
         "cpu_baseline": cpu,
         "parity": timed_parity,
         "breakdown_us": {
-            "norms_median": round(float(np.median(norms_ms)) * 1e3, 2),
-            "assign_median": round(float(np.median(assign_ms)) * 1e3, 2),
-            "assign_min": round(float(assign_ms.min()) * 1e3, 2),
-            "assign_p90": round(float(np.percentile(assign_ms, 90)) * 1e3, 2),
             "step_mean": round(ms_per_step * 1e3, 2),
+            "assign_launch_mean": round(assign_ms * 1e3, 2),
+            "norms_launch_mean": round(norms_ms * 1e3, 2),
         },
-        "assign_only_points_per_s": N / (float(np.median(assign_ms)) / 1e3),
+        "assign_only_points_per_s": N / (assign_ms / 1e3),
     }
     print(json.dumps(out), flush=True)
     if parity_reports:

@@ -789,7 +789,8 @@ constexpr int kMaxBucketLog2 = 2;    // S <= 4
 constexpr int64_t kMaxBinClusters = int64_t(kMaxBuckets) << kMaxBucketLog2;
 constexpr int kBucketThreads = 256;  // 4 waves
 constexpr int kBucketWaves = kBucketThreads / 64;
-constexpr int kBucketChunk = 512;    // slots resolved per round
+constexpr int kBucketChunk = 512;    // slots summed per round
+constexpr int kBucketSlots = 2048;   // a bucket up to this size has all its slot words in LDS
 constexpr int kSlotIdxBits = 24;     // a slot word: point index | cluster in bucket << 24
 static_assert(kMaxBinPoints <= (int64_t(1) << kSlotIdxBits), "point indices fit the slot word");
 
@@ -980,12 +981,13 @@ template <int V, int S>
 __global__ __launch_bounds__(kBucketThreads)
 void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ sidx,
                        const int32_t *__restrict__ dir,
-                       const uint16_t *__restrict__ C_old, int D, int K, int nb, int T, int tl,
+                       const uint16_t *__restrict__ C_old, int N, int D, int K, int nb, int T,
+                       int tl,
                        uint16_t *__restrict__ C_new, float *__restrict__ means,
                        float *__restrict__ norms, int32_t *__restrict__ counts) {
     extern __shared__ __attribute__((aligned(16))) int bdyn[];
-    __shared__ int ci[kBucketChunk];
-    __shared__ int wtot[kBucketWaves];
+    __shared__ int ci[kBucketSlots];
+    __shared__ int wtot[2][kBucketWaves];
     __shared__ int bcnt[kBucketWaves][S];
     __shared__ __attribute__((aligned(16))) uint16_t nrow[kBucketWaves][kMaxRow];
     const int tid = threadIdx.x;
@@ -999,60 +1001,121 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
     int *off = bdyn + kBucketWaves * S * D;                // [T + 1]
     int *src = off + T + 1;                                // [T]
 
-    // 1. Segments: thread r owns tiles 2r, 2r + 1 (T <= 512); the loads are
+    // 1. Segments: thread r owns tiles r and r + 256 (T <= 512), so that
+    // every wave holds tiles when T <= 256; the directory loads are
     // unconditional (clamped to tile T - 1) so they are in flight together,
     // and each takes a tile's two adjacent entries at once (8 bytes, 4-byte
-    // aligned, which global loads allow).
+    // aligned, which global loads allow).  The thread's own points (its two
+    // segments) are then loaded kPre at a time, so that their latency
+    // overlaps the scan; once the scan gives each segment its first slot
+    // they are placed in ci (when the whole bucket fits there).  Slots run in
+    // tile order: tiles 0..255 first, then 256..511, so the two halves are
+    // scanned side by side and the second is offset by the first's total.
     typedef int32_t i2 __attribute__((ext_vector_type(2)));
     constexpr int kTilesPerThread = kMaxBinTiles / kBucketThreads;
-    int seg[kTilesPerThread], sa[kTilesPerThread];
-    int sum = 0;
+    static_assert(kTilesPerThread == 2, "two segments per thread");
+    constexpr int kPre = 8;
+    int seg[kTilesPerThread] = {0, 0}, base[kTilesPerThread];
+    int wv[kPre];
+    // Sorted position of this thread's p-th point, p < seg[0] + seg[1].
+    auto word_pos = [&](int p) __attribute__((always_inline)) {
+        return p < seg[0] ? base[0] + p : base[1] + (p - seg[0]);
+    };
+    // Position read by a lane without a p-th point, the same on every lane
+    // of the wave (so a load costs one line request per real point plus at
+    // most one): the first point of the wave's lowest lane that has one, a
+    // line the wave reads anyway; in a wave with no points, a position that
+    // differs by wave and bucket, so that no one line is read by all waves.
+    int stand_in = 0;
     if (T > 0) {
 #pragma unroll
         for (int u = 0; u < kTilesPerThread; ++u) {
-            const int tt = min(tid * kTilesPerThread + u, T - 1);
+            const int tt = min(tid + u * kBucketThreads, T - 1);
             i2 pr;
             __builtin_memcpy(&pr, dir + static_cast<size_t>(tt) * ND + b, sizeof(pr));
-            sa[u] = pr.x;
-            seg[u] = pr.y;
+            seg[u] = tid + u * kBucketThreads < T ? pr.y - pr.x : 0;
+            base[u] = (tt << tl) + pr.x;
         }
+        // Unconditional loads (no branch to wait in).
+        const int sum = seg[0] + seg[1];
+        const uint64_t have = __ballot(sum > 0);
+        stand_in = have != 0 ? __builtin_amdgcn_readlane(word_pos(0), __builtin_ctzll(have))
+                             : min(b * 64 + w * 16, N - 1);
 #pragma unroll
-        for (int u = 0; u < kTilesPerThread; ++u) {
-            const int tt = tid * kTilesPerThread + u;
-            seg[u] = tt < T ? seg[u] - sa[u] : 0;
-            sum += seg[u];
-        }
+        for (int p = 0; p < kPre; ++p)
+            wv[p] = sidx[p < sum ? word_pos(p) : stand_in];
     }
-    int x = sum;
+    const int sum = seg[0] + seg[1];
+    int x[kTilesPerThread] = {seg[0], seg[1]};
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o)
-            x += y;
-    }
-    if (lane == 63)
-        wtot[w] = x;
-    __syncthreads();
-    int ex = x - sum;
-    for (int v2 = 0; v2 < w; ++v2)
-        ex += wtot[v2];
-    const int n_pts = wtot[0] + wtot[1] + wtot[2] + wtot[3];
 #pragma unroll
-    for (int u = 0; u < kTilesPerThread; ++u) {
-        const int tt = tid * kTilesPerThread + u;
-        if (tt < T) {
-            off[tt] = ex;
-            src[tt] = (tt << tl) + sa[u];
-            ex += seg[u];
+        for (int u = 0; u < kTilesPerThread; ++u) {
+            const int y = __shfl_up(x[u], o);
+            if (lane >= o)
+                x[u] += y;
         }
     }
-    if (tid == 0)
-        off[T] = n_pts;
+    if (lane == 63) {
+        wtot[0][w] = x[0];
+        wtot[1][w] = x[1];
+    }
+    __syncthreads();
+    int ex[kTilesPerThread], tot[kTilesPerThread];
+#pragma unroll
+    for (int u = 0; u < kTilesPerThread; ++u) {
+        ex[u] = x[u] - seg[u];
+        tot[u] = 0;
+#pragma unroll
+        for (int v2 = 0; v2 < kBucketWaves; ++v2) {
+            ex[u] += v2 < w ? wtot[u][v2] : 0;
+            tot[u] += wtot[u][v2];
+        }
+    }
+    ex[1] += tot[0];
+    const int n_pts = tot[0] + tot[1];
+    // Slot of this thread's p-th point.
+    auto slot_of = [&](int p) __attribute__((always_inline)) {
+        return p < seg[0] ? ex[0] + p : ex[1] + (p - seg[0]);
+    };
+    // Same for every thread of the workgroup (so are the barriers below that
+    // depend on it): the bucket's slot words all fit in ci.
+    const bool whole = n_pts <= kBucketSlots;
+    if (whole) {
+#pragma unroll
+        for (int p = 0; p < kPre; ++p)
+            if (p < sum)
+                ci[slot_of(p)] = wv[p];
+        for (int p0 = kPre; p0 < sum; p0 += kPre) {    // a thread with more points
+            int more[kPre];
+#pragma unroll
+            for (int p = 0; p < kPre; ++p)
+                more[p] = sidx[p0 + p < sum ? word_pos(p0 + p) : stand_in];
+#pragma unroll
+            for (int p = 0; p < kPre; ++p)
+                if (p0 + p < sum)
+                    ci[slot_of(p0 + p)] = more[p];
+        }
+    } else {
+        // Larger buckets resolve one chunk of slots at a time below: each
+        // slot finds its tile by binary search over the segments' first slots.
+#pragma unroll
+        for (int u = 0; u < kTilesPerThread; ++u) {
+            const int tt = tid + u * kBucketThreads;
+            if (tt < T) {
+                off[tt] = ex[u];
+                src[tt] = base[u];
+            }
+        }
+        if (tid == 0)
+            off[T] = n_pts;
+    }
     __syncthreads();
 
-    // 2. Sums.  A wave takes kRows slots at a time: lane u reads slot u's
-    // point index (and cluster) from LDS, the row loads take them by
-    // readlane as scalar bases, all kRows loads in flight together.
+    // 2. Sums, over chunks of 512 slots.  A wave takes kRows slots at a
+    // time: lane u reads slot u's word (point index, cluster) from LDS, the
+    // row loads take them by readlane as scalar bases, all kRows loads in
+    // flight together.
     constexpr int kSlotsPerThread = kBucketChunk / kBucketThreads;
     constexpr int kRows = V == 2 ? 32 : (V == 4 ? 16 : 8);
     float acc[S][V];
@@ -1066,36 +1129,39 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
     }
     for (int c0 = 0; c0 < n_pts; c0 += kBucketChunk) {
         const int nc = min(kBucketChunk, n_pts - c0);
-        int sp[kSlotsPerThread];
+        const int *words = whole ? ci + c0 : ci;
+        if (!whole) {
+            int sp[kSlotsPerThread];
 #pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
-            const int slot = c0 + min(tid + u * kBucketThreads, nc - 1);
-            int lo = 0, hi = T - 1;                // last tile whose segment starts <= slot
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= slot)
-                    lo = mid;
-                else
-                    hi = mid - 1;
+            for (int u = 0; u < kSlotsPerThread; ++u) {
+                const int slot = c0 + min(tid + u * kBucketThreads, nc - 1);
+                int lo = 0, hi = T - 1;                // last tile whose segment starts <= slot
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (off[mid] <= slot)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                sp[u] = src[lo] + (slot - off[lo]);
             }
-            sp[u] = src[lo] + (slot - off[lo]);
-        }
-        int li[kSlotsPerThread];
+            int li[kSlotsPerThread];
 #pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u)
-            li[u] = sidx[sp[u]];
+            for (int u = 0; u < kSlotsPerThread; ++u)
+                li[u] = sidx[sp[u]];
 #pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
-            const int j = tid + u * kBucketThreads;
-            if (j < nc)
-                ci[j] = li[u];
+            for (int u = 0; u < kSlotsPerThread; ++u) {
+                const int j = tid + u * kBucketThreads;
+                if (j < nc)
+                    ci[j] = li[u];
+            }
+            __syncthreads();
         }
-        __syncthreads();
         const int j0 = nc * w / kBucketWaves;
         const int j1 = nc * (w + 1) / kBucketWaves;
         for (int jb = j0; jb < j1; jb += kRows) {
             const int jj = min(jb + (kRows == 64 ? lane : lane % kRows), j1 - 1);
-            const int word = ci[jj];
+            const int word = words[jj];
             const int my_i = word & ((1 << kSlotIdxBits) - 1);
             const int my_c = S > 1 ? word >> kSlotIdxBits : 0;
             RowBits<V> r[kRows];
@@ -1120,7 +1186,8 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
                 }
             }
         }
-        __syncthreads();
+        if (!whole)
+            __syncthreads();                       // ci is refilled for the next chunk
     }
 
     // 3. Partials of the four waves to LDS; cluster c's sum adds them in
@@ -1173,29 +1240,29 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
 
 template <int V, int S>
 hipError_t launch_bucket_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *sidx,
-                              const int32_t *dir, const uint16_t *C_old, int D, int K,
+                              const int32_t *dir, const uint16_t *C_old, int N, int D, int K,
                               uint16_t *C_new, float *norms, int32_t *counts, float *means,
                               hipStream_t stream) {
     const size_t lds = (static_cast<size_t>(kBucketWaves) * S * D +
                         2 * static_cast<size_t>(pl.bin_tiles) + 1) * 4;
     hipLaunchKernelGGL((upd_bucket_kernel<V, S>), dim3(pl.buckets), dim3(kBucketThreads), lds,
-                       stream, X, sidx, dir, C_old, D, K, pl.buckets, pl.bin_tiles,
+                       stream, X, sidx, dir, C_old, N, D, K, pl.buckets, pl.bin_tiles,
                        pl.bin_tile_log2, C_new, means, norms, counts);
     return hipGetLastError();
 }
 
 template <int V>
 hipError_t launch_bucket_v(const UpdatePlan &pl, const uint16_t *X, const int32_t *sidx,
-                           const int32_t *dir, const uint16_t *C_old, int D, int K,
+                           const int32_t *dir, const uint16_t *C_old, int N, int D, int K,
                            uint16_t *C_new, float *norms, int32_t *counts, float *means,
                            hipStream_t stream) {
     if (pl.bucket_log2 == 0)
-        return launch_bucket_sums<V, 1>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
+        return launch_bucket_sums<V, 1>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
                                         means, stream);
     if (pl.bucket_log2 == 1)
-        return launch_bucket_sums<V, 2>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
+        return launch_bucket_sums<V, 2>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
                                         means, stream);
-    return launch_bucket_sums<V, 4>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
+    return launch_bucket_sums<V, 4>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
                                     means, stream);
 }
 
@@ -1324,12 +1391,12 @@ hipError_t launch_update(const UpdatePlan &pl, const uint16_t *X, const int32_t 
                 return e;
         }
         if (D <= 128)
-            return launch_bucket_v<2>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
+            return launch_bucket_v<2>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
                                       means, stream);
         if (D <= 256)
-            return launch_bucket_v<4>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
+            return launch_bucket_v<4>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
                                       means, stream);
-        return launch_bucket_v<8>(pl, X, sidx, dir, C_old, D, K, C_new, norms, counts,
+        return launch_bucket_v<8>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
                                   means, stream);
     }
     int32_t *start = nullptr, *end = nullptr, *keys = nullptr, *vals = nullptr;

@@ -105,6 +105,22 @@ def test_more_than_two_million_points(path):
     assert st["clusters"] == K
 
 
+@PATHS
+def test_buckets_around_the_lds_slot_list(path):
+    """About 2000 points per bucket of one cluster: most buckets keep all
+    their slot words in LDS (four chunks of sums), those above 2048 take the
+    chunk-by-chunk resolution, in the same call; each bucket workgroup
+    thread owns ~8 points of two tiles, so some take a second round of
+    slot-word loads."""
+    N, D, K = 520_000, 16, 256
+    X, C, a = W.gaussian_mixture(N, D, K, 82)
+    lab = noisy_labels(a, K, 82)
+    sizes = np.bincount(lab[(lab >= 0) & (lab < K)], minlength=K)
+    assert sizes.max() > 2048 and (sizes <= 2048).sum() > K // 2
+    st = check(X, lab, C, run_update(X, lab, C, path=path))
+    assert st["clusters"] == K
+
+
 @functools.lru_cache(maxsize=1)
 def _largest_bucket_path_set():
     N, D, K = 1 << 24, 16, 4096

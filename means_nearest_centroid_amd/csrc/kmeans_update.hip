@@ -766,8 +766,9 @@ void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__rest
 //     bucket starts in the tile (dir[tile][bucket]).  No global offsets: a
 //     bucket's points are the concatenation, over tiles in order, of one
 //     segment per tile, which is already index order.
-//  b. upd_bucket_kernel: one workgroup per bucket walks those segments in
-//     tile order, in chunks of 512 slots; each of its four waves sums a fixed
+//  b. upd_bucket_kernel: one workgroup per bucket gathers those segments'
+//     slot words (point index, cluster in bucket) in tile order into LDS and
+//     walks them in chunks of 512 slots; each of its four waves sums a fixed
 //     quarter of every chunk's slots in order into per-cluster registers, the
 //     four partials are added in wave order, and the workgroup finishes its S
 //     clusters (empty ones keep their rows).  The order of every sum depends
@@ -975,8 +976,9 @@ __device__ __forceinline__ int xcd_contiguous(int i, int n) {
 }
 
 // One workgroup per bucket b (clusters b S .. b S + S - 1).  Dynamic LDS:
-// the four waves' S x D partial sums, then off[T + 1] (first slot of each
-// tile's segment) and src[T] (its first sorted position).
+// the four waves' S x D partial sums, then, for a bucket of more than 2048
+// points, off[T + 1] (first slot of each tile's segment) and src[T] (its
+// first sorted position).
 template <int V, int S>
 __global__ __launch_bounds__(kBucketThreads)
 void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ sidx,

@@ -95,7 +95,7 @@ def _counter_per_dispatch(csv_path: str, counter: str):
     kernels together), the counter's total over all dispatches and the number
     of dispatches, from a rocprofv3 --pmc counter_collection.csv; for the
     update, the dispatches of its last kernel (one per call: the finish kernel
-    of the sort path or the bucket kernel)."""
+    of the sort path or either bucket kernel)."""
     import csv
     import collections
     tot = collections.defaultdict(float)
@@ -109,7 +109,8 @@ def _counter_per_dispatch(csv_path: str, counter: str):
             if kind is None:
                 continue
             tot[kind] += float(row["Counter_Value"])
-            if kind != "update" or "upd_finish_kernel" in name or "upd_bucket_kernel" in name:
+            if kind != "update" or any(k in name for k in ("upd_finish_kernel", "upd_bucket_kernel",
+                                                            "upd_bucket_runs_kernel")):
                 disp[kind].add(row["Dispatch_Id"])
     return {k: tot[k] / len(disp[k]) for k in tot}
 

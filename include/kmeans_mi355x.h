@@ -207,9 +207,8 @@ kmeans_status_t kmeans_plan(int64_t N, int64_t D, int64_t K, int32_t compute_uni
  * about 16 bytes per point plus 8 bytes per cluster is the stream's
  * workspace (see kmeans_release_workspace); KMEANS_ERR_NO_MEMORY if it
  * cannot grow.  The path is chosen from the shape (kmeans_update_path with
- * KMEANS_UPDATE_AUTO): buckets when 256 <= K <= 4096 and N <= 2^24,
- * else
- * the radix sort.
+ * KMEANS_UPDATE_AUTO): buckets when 256 <= K <= 16384 and N <= 2^24,
+ * else the radix sort.
  */
 kmeans_status_t kmeans_update(const void *X, const int32_t *labels, const void *C_old,
                               int64_t N, int64_t D, int64_t K, void *C_new, float *norms,
@@ -224,14 +223,17 @@ typedef enum {
      * workgroups.  Per radix pass a histogram and a scatter launch (and a
      * scan launch when N is over 2^21), then the reduce and the finish. */
     KMEANS_UPDATE_SORT = 1,
-    /* Clusters grouped into at most 1024 buckets of 1, 2 or 4 clusters;
-     * each tile of 1024 or more points sorts its own points by bucket,
-     * stably, and records where each bucket starts in it; then one
+    /* Clusters grouped into at most 1024 buckets of 1, 2, 4, 8 or 16
+     * clusters; each tile of 1024 or more points sorts its own points by
+     * bucket, stably, and records where each bucket starts in it; then one
      * workgroup per bucket gathers its points tile by tile and sums their
-     * rows in index order (four waves each sum a fixed quarter of every 512
-     * points, added in wave order).  Two launches.  N <= 2^24 and K <= 4096
-     * (else KMEANS_ERR_UNSUPPORTED); a bucket holding a large share of all
-     * points runs on one compute unit, far slower than the sort path. */
+     * rows in index order (buckets of up to 4 clusters: four waves each sum
+     * a fixed quarter of every 512 points, added in wave order; of 8 or 16:
+     * every 512 points are sorted by cluster, stably, and a cluster's rows
+     * are summed by one wave, chunk after chunk).  Two launches.  N <= 2^24
+     * and K <= 16384 (else KMEANS_ERR_UNSUPPORTED); a bucket holding a large
+     * share of all points runs on one compute unit, far slower than the
+     * sort path. */
     KMEANS_UPDATE_BUCKETS = 2
 } kmeans_update_path_t;
 

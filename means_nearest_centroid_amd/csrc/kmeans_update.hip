@@ -757,9 +757,9 @@ void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__rest
 
 // ---- 4. bucket path: a tile-local sort and one workgroup per bucket ------
 //
-// For K up to 4096 and N up to 2^24 (the common Lloyd shapes), two launches
+// For K up to 16384 and N up to 2^24 (the common Lloyd shapes), two launches
 // replace the radix passes, the reduce and the finish kernels.  Clusters are
-// grouped into nb <= 1024 buckets of S = 2^s clusters (bucket k >> s).
+// grouped into nb <= 1024 buckets of S = 2^s <= 16 clusters (bucket k >> s).
 //
 //  a. upd_bin_kernel: every tile of 2^tl points sorts its own points by
 //     bucket, stably (index order inside a bucket), and records where each
@@ -771,8 +771,10 @@ void upd_finish_kernel(const uint16_t *__restrict__ C_old, const int32_t *__rest
 //     walks them in chunks of 512 slots; each of its four waves sums a fixed
 //     quarter of every chunk's slots in order into per-cluster registers, the
 //     four partials are added in wave order, and the workgroup finishes its S
-//     clusters (empty ones keep their rows).  The order of every sum depends
-//     only on the data, so a call gives the same bits every time.
+//     clusters (empty ones keep their rows).  Buckets of 8 or 16 clusters
+//     take upd_bucket_runs_kernel instead, which sorts the words by cluster
+//     first.  The order of every sum depends only on the data, so a call
+//     gives the same bits every time.
 //
 // A bucket is summed by one workgroup, so a bucket holding a large share of
 // all points runs on one CU (correct, but far slower than the radix path,
@@ -786,7 +788,7 @@ constexpr int kScanThreads2 = 256;   // threads of the bin scan: 4 buckets each
 constexpr int kBinDigitsPerThread = kMaxBuckets / kScanThreads2;   // one 16-byte group
 constexpr int kMaxBinTiles = 512;
 constexpr int64_t kMaxBinPoints = int64_t(1) << 24;
-constexpr int kMaxBucketLog2 = 2;    // S <= 4
+constexpr int kMaxBucketLog2 = 4;    // S <= 16
 constexpr int64_t kMaxBinClusters = int64_t(kMaxBuckets) << kMaxBucketLog2;
 constexpr int kBucketThreads = 256;  // 4 waves
 constexpr int kBucketWaves = kBucketThreads / 64;
@@ -794,6 +796,7 @@ constexpr int kBucketChunk = 512;    // slots summed per round
 constexpr int kBucketSlots = 2048;   // a bucket up to this size has all its slot words in LDS
 constexpr int kSlotIdxBits = 24;     // a slot word: point index | cluster in bucket << 24
 static_assert(kMaxBinPoints <= (int64_t(1) << kSlotIdxBits), "point indices fit the slot word");
+static_assert(kSlotIdxBits + kMaxBucketLog2 <= 31, "the cluster in its bucket fits the slot word");
 
 // Tile t: positions [t << tl, min(N, (t + 1) << tl)).  Wave w owns the
 // contiguous eighth [w q, (w + 1) q) of the tile (q = 2^tl / 8), so the
@@ -975,35 +978,27 @@ __device__ __forceinline__ int xcd_contiguous(int i, int n) {
     return x * q + min(x, r) + i / kXcds;
 }
 
-// One workgroup per bucket b (clusters b S .. b S + S - 1).  Dynamic LDS:
-// the four waves' S x D partial sums, then, for a bucket of more than 2048
-// points, off[T + 1] (first slot of each tile's segment) and src[T] (its
-// first sorted position).
-template <int V, int S>
-__global__ __launch_bounds__(kBucketThreads)
-void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ sidx,
-                       const int32_t *__restrict__ dir,
-                       const uint16_t *__restrict__ C_old, int N, int D, int K, int nb, int T,
-                       int tl,
-                       uint16_t *__restrict__ C_new, float *__restrict__ means,
-                       float *__restrict__ norms, int32_t *__restrict__ counts) {
-    extern __shared__ __attribute__((aligned(16))) int bdyn[];
-    __shared__ int ci[kBucketSlots];
-    __shared__ int wtot[2][kBucketWaves];
-    __shared__ int bcnt[kBucketWaves][S];
-    __shared__ __attribute__((aligned(16))) uint16_t nrow[kBucketWaves][kMaxRow];
+// Bucket b's slot words (point index, cluster in bucket) in slot order,
+// i.e. tile order, for a workgroup of kBucketThreads threads; every thread
+// calls it.  A bucket of at most kBucketSlots points gets all its words in
+// ci; a larger one gets off[0..T] (first slot of each tile's segment) and
+// src[0..T) (its first sorted position) for chunk_words.  Ends with a
+// barrier.
+struct SlotWords {
+    int n_pts;     // points in the bucket
+    bool whole;    // all their words are in ci (the same on every thread)
+};
+
+__device__ __forceinline__ SlotWords gather_slot_words(const int32_t *__restrict__ sidx,
+                                                       const int32_t *__restrict__ dir, int N,
+                                                       int nb, int T, int tl, int b, int *ci,
+                                                       int (*wtot)[kBucketWaves], int *off,
+                                                       int *src) {
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
-    const int b = xcd_contiguous(blockIdx.x, nb);
-    const bool on = lane * V < D;
-    const int col = on ? lane * V : 0;             // idle lanes load column 0
     const int ND = nb + 1;
-    float *part = reinterpret_cast<float *>(bdyn);         // [4][S][D]
-    int *off = bdyn + kBucketWaves * S * D;                // [T + 1]
-    int *src = off + T + 1;                                // [T]
-
-    // 1. Segments: thread r owns tiles r and r + 256 (T <= 512), so that
+    // Thread r owns tiles r and r + 256 (T <= 512), so that
     // every wave holds tiles when T <= 256; the directory loads are
     // unconditional (clamped to tile T - 1) so they are in flight together,
     // and each takes a tile's two adjacent entries at once (8 bytes, 4-byte
@@ -1113,12 +1108,84 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
             off[T] = n_pts;
     }
     __syncthreads();
+    return SlotWords{n_pts, whole};
+}
+
+// Words of slots [c0, c0 + nc) of a gathered bucket: in place in ci when the
+// whole bucket is there, else resolved into ci[0, nc) (each slot finds its
+// tile by binary search over the segments' first slots).  Every thread
+// calls it; the second case ends with a barrier, and the caller must reach
+// one more before ci is resolved again.
+__device__ __forceinline__ const int *chunk_words(const SlotWords &sw, int c0, int nc, int T,
+                                                  const int *off, const int *src,
+                                                  const int32_t *__restrict__ sidx, int *ci) {
+    if (sw.whole)
+        return ci + c0;
+    constexpr int kSlotsPerThread = kBucketChunk / kBucketThreads;
+    const int tid = threadIdx.x;
+    int sp[kSlotsPerThread];
+#pragma unroll
+    for (int u = 0; u < kSlotsPerThread; ++u) {
+        const int slot = c0 + min(tid + u * kBucketThreads, nc - 1);
+        int lo = 0, hi = T - 1;                    // last tile whose segment starts <= slot
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= slot)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        sp[u] = src[lo] + (slot - off[lo]);
+    }
+    int li[kSlotsPerThread];
+#pragma unroll
+    for (int u = 0; u < kSlotsPerThread; ++u)
+        li[u] = sidx[sp[u]];
+#pragma unroll
+    for (int u = 0; u < kSlotsPerThread; ++u) {
+        const int j = tid + u * kBucketThreads;
+        if (j < nc)
+            ci[j] = li[u];
+    }
+    __syncthreads();
+    return ci;
+}
+
+// One workgroup per bucket b (clusters b S .. b S + S - 1).  Dynamic LDS:
+// the four waves' S x D partial sums, then, for a bucket of more than 2048
+// points, off[T + 1] (first slot of each tile's segment) and src[T] (its
+// first sorted position).
+template <int V, int S>
+__global__ __launch_bounds__(kBucketThreads)
+void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ sidx,
+                       const int32_t *__restrict__ dir,
+                       const uint16_t *__restrict__ C_old, int N, int D, int K, int nb, int T,
+                       int tl,
+                       uint16_t *__restrict__ C_new, float *__restrict__ means,
+                       float *__restrict__ norms, int32_t *__restrict__ counts) {
+    extern __shared__ __attribute__((aligned(16))) int bdyn[];
+    __shared__ int ci[kBucketSlots];
+    __shared__ int wtot[2][kBucketWaves];
+    __shared__ int bcnt[kBucketWaves][S];
+    __shared__ __attribute__((aligned(16))) uint16_t nrow[kBucketWaves][kMaxRow];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int b = xcd_contiguous(blockIdx.x, nb);
+    const bool on = lane * V < D;
+    const int col = on ? lane * V : 0;             // idle lanes load column 0
+    float *part = reinterpret_cast<float *>(bdyn);         // [4][S][D]
+    int *off = bdyn + kBucketWaves * S * D;                // [T + 1]
+    int *src = off + T + 1;                                // [T]
+
+    // 1. The bucket's slot words.
+    const SlotWords sw = gather_slot_words(sidx, dir, N, nb, T, tl, b, ci, wtot, off, src);
+    const int n_pts = sw.n_pts;
 
     // 2. Sums, over chunks of 512 slots.  A wave takes kRows slots at a
     // time: lane u reads slot u's word (point index, cluster) from LDS, the
     // row loads take them by readlane as scalar bases, all kRows loads in
     // flight together.
-    constexpr int kSlotsPerThread = kBucketChunk / kBucketThreads;
     constexpr int kRows = V == 2 ? 32 : (V == 4 ? 16 : 8);
     float acc[S][V];
     int cw[S];
@@ -1131,34 +1198,7 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
     }
     for (int c0 = 0; c0 < n_pts; c0 += kBucketChunk) {
         const int nc = min(kBucketChunk, n_pts - c0);
-        const int *words = whole ? ci + c0 : ci;
-        if (!whole) {
-            int sp[kSlotsPerThread];
-#pragma unroll
-            for (int u = 0; u < kSlotsPerThread; ++u) {
-                const int slot = c0 + min(tid + u * kBucketThreads, nc - 1);
-                int lo = 0, hi = T - 1;                // last tile whose segment starts <= slot
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (off[mid] <= slot)
-                        lo = mid;
-                    else
-                        hi = mid - 1;
-                }
-                sp[u] = src[lo] + (slot - off[lo]);
-            }
-            int li[kSlotsPerThread];
-#pragma unroll
-            for (int u = 0; u < kSlotsPerThread; ++u)
-                li[u] = sidx[sp[u]];
-#pragma unroll
-            for (int u = 0; u < kSlotsPerThread; ++u) {
-                const int j = tid + u * kBucketThreads;
-                if (j < nc)
-                    ci[j] = li[u];
-            }
-            __syncthreads();
-        }
+        const int *words = chunk_words(sw, c0, nc, T, off, src, sidx, ci);
         const int j0 = nc * w / kBucketWaves;
         const int j1 = nc * (w + 1) / kBucketWaves;
         for (int jb = j0; jb < j1; jb += kRows) {
@@ -1188,7 +1228,7 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
                 }
             }
         }
-        if (!whole)
+        if (!sw.whole)
             __syncthreads();                       // ci is refilled for the next chunk
     }
 
@@ -1240,16 +1280,267 @@ void upd_bucket_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict
     }
 }
 
+// Buckets of S = 8 or 16 clusters (K up to 16384).  Choosing each row's
+// cluster among S register accumulators would cost an S-way choice per row,
+// so the bucket's slot words are first sorted by cluster in LDS (stably, so
+// a cluster's slots keep index order; a bucket of more than 2048 points
+// chunk by chunk, 512 slots at a time) and each wave walks a fixed quarter
+// of the sorted piece with one accumulator, closing a run when the cluster
+// changes.  A run inside the wave's quarter goes straight to its cluster's
+// LDS sum (no other wave has that cluster in the piece); the quarter's first
+// and last runs, which may continue in the neighbouring quarters, go to
+// edge rows that wave 0 adds in slot order once all waves are done.  A
+// cluster's sum is thus its run pieces added left to right in slot order,
+// piece after piece, each summed in index order: the same bits on every
+// call, whatever the cluster sizes.  Dynamic LDS: the S x D sums, the 4 x 2
+// x D edge rows, then, for a bucket of more than 2048 points, off[T + 1]
+// and src[T] (as in upd_bucket_kernel).
+template <int V, int S>
+__global__ __launch_bounds__(kBucketThreads)
+__attribute__((amdgpu_waves_per_eu(kBucketWaves, kBucketWaves)))   // four workgroups per CU
+void upd_bucket_runs_kernel(const uint16_t *__restrict__ X, const int32_t *__restrict__ sidx,
+                            const int32_t *__restrict__ dir, const uint16_t *__restrict__ C_old,
+                            int N, int D, int K, int nb, int T, int tl,
+                            uint16_t *__restrict__ C_new, float *__restrict__ means,
+                            float *__restrict__ norms, int32_t *__restrict__ counts) {
+    static_assert(S == 8 || S == 16, "buckets of eight or sixteen clusters");
+    constexpr int kKeyBits = S == 8 ? 3 : 4;
+    constexpr int kWordsPerThread = kBucketSlots / kBucketThreads;
+    constexpr int kGroups = kWordsPerThread * kBucketWaves;   // 64-slot groups of a sort
+    constexpr int kRows = V == 2 ? 32 : (V == 4 ? 16 : 8);
+    extern __shared__ __attribute__((aligned(16))) int bdyn[];
+    __shared__ int ci[kBucketSlots];
+    __shared__ int sorted[kBucketSlots];
+    __shared__ int wtot[2][kBucketWaves];
+    __shared__ int grp[kGroups][S];                // per (group, key): count, then first position
+    __shared__ int ccount[S];                      // points of each cluster, all chunks
+    __shared__ int edge_c[kBucketWaves][2];        // cluster of each edge row, -1 if none
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int b = xcd_contiguous(blockIdx.x, nb);
+    const bool on = lane * V < D;
+    const int col = on ? lane * V : 0;             // idle lanes load column 0
+    float *sums = reinterpret_cast<float *>(bdyn);         // [S][D]
+    float *edge = sums + S * D;                            // [4][2][D]
+    // The outputs' row copies (one row of D bf16 per wave) reuse the edge
+    // rows, which are done with by then.
+    uint16_t *nrow = reinterpret_cast<uint16_t *>(edge);
+    int *off = bdyn + (S + 2 * kBucketWaves) * D;          // [T + 1]
+    int *src = off + T + 1;                                // [T]
+    // Cleared here; the barrier that ends the gather orders this before use.
+    for (int i = tid; i < S * D; i += kBucketThreads)
+        sums[i] = 0.0f;
+    if (tid < S)
+        ccount[tid] = 0;
+
+    // 1. The bucket's slot words.
+    const SlotWords sw = gather_slot_words(sidx, dir, N, nb, T, tl, b, ci, wtot, off, src);
+
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    // A bucket whose words are all in ci is sorted and summed in one piece;
+    // a larger one in chunks of 512 slots.
+    const int piece = sw.whole ? max(sw.n_pts, 1) : kBucketChunk;
+    for (int c0 = 0; c0 < sw.n_pts; c0 += piece) {
+        const int nc = min(piece, sw.n_pts - c0);
+        const int *words = chunk_words(sw, c0, nc, T, off, src, sidx, ci);
+
+        // 2. Stable counting sort of the piece by key (the cluster in the
+        // bucket).  Slot u * 256 + tid lies in group u * 4 + w, groups in
+        // slot order; inside a group a slot's rank among its key's slots
+        // comes from one ballot per key bit, and the key's last lane
+        // records the group's count.
+        const int ng = (nc + 63) / 64;             // groups holding slots
+        for (int i = tid; i < ng * S; i += kBucketThreads)
+            (&grp[0][0])[i] = 0;
+        __syncthreads();
+        // Key of a slot word: its cluster in the bucket.
+        auto key_of = [](int word) __attribute__((always_inline)) {
+            return static_cast<int>(static_cast<uint32_t>(word) >> kSlotIdxBits);
+        };
+        int wd[kWordsPerThread], rank[kWordsPerThread];
+#pragma unroll
+        for (int u = 0; u < kWordsPerThread; ++u) {
+            if (u * kBucketThreads >= nc)
+                break;                             // uniform
+            const int j = u * kBucketThreads + tid;
+            const bool valid = j < nc;
+            wd[u] = valid ? words[j] : 0;
+            const int key = key_of(wd[u]);
+            uint64_t same = __ballot(valid);
+#pragma unroll
+            for (int bit = 0; bit < kKeyBits; ++bit) {
+                const bool one = (key >> bit) & 1;
+                const uint64_t m = __ballot(valid && one);
+                same &= one ? m : ~m;
+            }
+            rank[u] = __popcll(same & below);
+            if (valid && (same >> lane) == 1)
+                grp[u * kBucketWaves + w][key] = rank[u] + 1;
+        }
+        __syncthreads();
+        // Exclusive scan over (key, group), key-major: lane k of wave 0 owns
+        // key (cluster) k; the piece's cluster counts are added to the
+        // totals.
+        if (w == 0) {
+            int t = 0;
+            if (lane < S)
+                for (int g = 0; g < ng; ++g)
+                    t += grp[g][lane];
+            int x = t;
+#pragma unroll
+            for (int o = 1; o < S; o <<= 1) {
+                const int y = __shfl_up(x, o);
+                if (lane >= o)
+                    x += y;
+            }
+            if (lane < S) {
+                int st = x - t;
+                for (int g = 0; g < ng; ++g) {
+                    const int cnt = grp[g][lane];
+                    grp[g][lane] = st;
+                    st += cnt;
+                }
+                ccount[lane] += t;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kWordsPerThread; ++u) {
+            if (u * kBucketThreads >= nc)
+                break;                             // uniform
+            if (u * kBucketThreads + tid < nc)
+                sorted[grp[u * kBucketWaves + w][key_of(wd[u])] + rank[u]] = wd[u];
+        }
+        __syncthreads();
+
+        // 3. Sums: wave w walks sorted positions [j0, j1), kRows rows at a
+        // time, rows loaded by readlane of the point index.
+        const int j0 = nc * w / kBucketWaves;
+        const int j1 = nc * (w + 1) / kBucketWaves;
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            acc[v] = 0.0f;
+        int cur = -1;                              // cluster of the open run (uniform)
+        int runs = 0;                              // runs closed so far (uniform)
+        // Closes the open run: the quarter's first run to edge row 0, any
+        // later one to its cluster's sum; the last run is closed after the
+        // loop, to edge row 1.
+        auto close_run = [&](bool last) __attribute__((always_inline)) {
+            const int e = runs == 0 ? 0 : (last ? 1 : -1);
+            if (on) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    if (e >= 0)
+                        edge[(w * 2 + e) * D + lane * V + v] = acc[v];
+                    else
+                        sums[cur * D + lane * V + v] += acc[v];
+                }
+            }
+            if (e >= 0 && lane == 0)
+                edge_c[w][e] = cur;
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                acc[v] = 0.0f;
+            ++runs;
+        };
+        if (lane == 0) {
+            edge_c[w][0] = -1;
+            edge_c[w][1] = -1;
+        }
+        for (int jb = j0; jb < j1; jb += kRows) {
+            const int jj = min(jb + lane % kRows, j1 - 1);
+            const int word = sorted[jj];
+            const int my_i = word & ((1 << kSlotIdxBits) - 1);
+            const int my_c = static_cast<int>(static_cast<uint32_t>(word) >> kSlotIdxBits);
+            RowBits<V> r[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                const int i = __builtin_amdgcn_readlane(my_i, u);
+                r[u] = load_row<V>(X + static_cast<size_t>(i) * D + col);
+            }
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                if (jb + u < j1) {                 // uniform
+                    const int c = __builtin_amdgcn_readlane(my_c, u);
+                    if (c != cur) {                // uniform
+                        if (cur >= 0)
+                            close_run(false);
+                        cur = c;
+                    }
+#pragma unroll
+                    for (int v = 0; v < V; ++v)
+                        acc[v] += row_value<V>(r[u], v);
+                }
+            }
+        }
+        if (cur >= 0)
+            close_run(true);
+        __syncthreads();
+        // Edge rows in slot order: wave by wave, its first run then its last.
+        if (w == 0 && on) {
+            for (int q = 0; q < kBucketWaves * 2; ++q) {
+                const int c = edge_c[q >> 1][q & 1];
+                if (c >= 0) {
+#pragma unroll
+                    for (int v = 0; v < V; ++v)
+                        sums[c * D + lane * V + v] += edge[q * D + lane * V + v];
+                }
+            }
+        }
+        // sorted, grp, the edge rows and their clusters are rewritten by the
+        // next chunk; the sums are read below.
+        __syncthreads();
+    }
+
+    // 4. Outputs: wave w finishes clusters b S + w, b S + w + 4, ...
+    for (int c = w; c < S; c += kBucketWaves) {
+        const int64_t kk = static_cast<int64_t>(b) * S + c;
+        if (kk >= K)
+            break;
+        const int k = static_cast<int>(kk);
+        const int count = ccount[c];
+        if (count == 0) {
+            uint32_t bits[V];
+            float mean[V];
+            RowBits<V> r = on ? load_row<V>(C_old + static_cast<size_t>(k) * D + lane * V)
+                              : RowBits<V>{};
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                mean[v] = row_value<V>(r, v);
+                bits[v] = __float_as_uint(mean[v]) >> 16;
+            }
+            emit_cluster<V>(k, bits, mean, 0, D, lane, nrow + w * D, C_new, means, norms, counts);
+        } else {
+            float s2[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                s2[v] = on ? sums[c * D + lane * V + v] : 0.0f;
+            emit_mean<V>(k, s2, count, D, lane, nrow + w * D, C_new, means, norms, counts);
+        }
+    }
+}
+
 template <int V, int S>
 hipError_t launch_bucket_sums(const UpdatePlan &pl, const uint16_t *X, const int32_t *sidx,
                               const int32_t *dir, const uint16_t *C_old, int N, int D, int K,
                               uint16_t *C_new, float *norms, int32_t *counts, float *means,
                               hipStream_t stream) {
-    const size_t lds = (static_cast<size_t>(kBucketWaves) * S * D +
-                        2 * static_cast<size_t>(pl.bin_tiles) + 1) * 4;
-    hipLaunchKernelGGL((upd_bucket_kernel<V, S>), dim3(pl.buckets), dim3(kBucketThreads), lds,
-                       stream, X, sidx, dir, C_old, N, D, K, pl.buckets, pl.bin_tiles,
-                       pl.bin_tile_log2, C_new, means, norms, counts);
+    if constexpr (S <= 4) {
+        const size_t lds = (static_cast<size_t>(kBucketWaves) * S * D +
+                            2 * static_cast<size_t>(pl.bin_tiles) + 1) * 4;
+        hipLaunchKernelGGL((upd_bucket_kernel<V, S>), dim3(pl.buckets), dim3(kBucketThreads),
+                           lds, stream, X, sidx, dir, C_old, N, D, K, pl.buckets, pl.bin_tiles,
+                           pl.bin_tile_log2, C_new, means, norms, counts);
+    } else {
+        const size_t lds = ((static_cast<size_t>(S) + 2 * kBucketWaves) * D +
+                            2 * static_cast<size_t>(pl.bin_tiles) + 1) * 4;
+        hipLaunchKernelGGL((upd_bucket_runs_kernel<V, S>), dim3(pl.buckets),
+                           dim3(kBucketThreads), lds, stream, X, sidx, dir, C_old, N, D, K,
+                           pl.buckets, pl.bin_tiles, pl.bin_tile_log2, C_new, means, norms,
+                           counts);
+    }
     return hipGetLastError();
 }
 
@@ -1264,8 +1555,14 @@ hipError_t launch_bucket_v(const UpdatePlan &pl, const uint16_t *X, const int32_
     if (pl.bucket_log2 == 1)
         return launch_bucket_sums<V, 2>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
                                         means, stream);
-    return launch_bucket_sums<V, 4>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
-                                    means, stream);
+    if (pl.bucket_log2 == 2)
+        return launch_bucket_sums<V, 4>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
+                                        means, stream);
+    if (pl.bucket_log2 == 3)
+        return launch_bucket_sums<V, 8>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
+                                        means, stream);
+    return launch_bucket_sums<V, 16>(pl, X, sidx, dir, C_old, N, D, K, C_new, norms, counts,
+                                     means, stream);
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }

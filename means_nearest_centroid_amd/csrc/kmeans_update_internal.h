@@ -31,7 +31,7 @@ struct UpdatePlan {
     int compute_units; // reduce workgroups: four per CU
 };
 
-// Whether the bucket path supports the shape (N <= 2^24, K <= 4096).
+// Whether the bucket path supports the shape (N <= 2^24, K <= 16384).
 bool bucket_path_fits(int64_t N, int64_t K);
 
 // Requires 0 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller);

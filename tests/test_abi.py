@@ -250,7 +250,7 @@ def test_update_rejects_bad_arguments(lib, kw, status):
     (dict(), -1, km.KMEANS_ERR_INVALID_ARG),
     (dict(), 3, km.KMEANS_ERR_INVALID_ARG),
     (dict(N=(1 << 24) + 1), km.UPDATE_BUCKETS, km.KMEANS_ERR_UNSUPPORTED),
-    (dict(K=4097), km.UPDATE_BUCKETS, km.KMEANS_ERR_UNSUPPORTED),
+    (dict(K=16385), km.UPDATE_BUCKETS, km.KMEANS_ERR_UNSUPPORTED),
     (dict(X=NUL), km.UPDATE_BUCKETS, km.KMEANS_ERR_INVALID_ARG),
 ])
 def test_update_path_rejects_bad_arguments(lib, kw, path, status):

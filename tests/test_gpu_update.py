@@ -85,7 +85,7 @@ SMALL = [  # (N, D, K): ragged everywhere, K > N, 1, 2 and 3 radix passes,
 @PATHS
 @pytest.mark.parametrize("N,D,K", SMALL)
 def test_small_shapes(N, D, K, path):
-    if path == 2 and K > 4096:
+    if path == 2 and K > 16384:
         pytest.skip("K over the bucket path's limit (covered by the sort path)")
     X, C, a = W.gaussian_mixture(N, D, K, 300 + N + K)
     lab = noisy_labels(a, K, N)
@@ -239,7 +239,7 @@ def test_nonfinite_points(path):
 def test_workload_full(cfg, path):
     X, C, meta = W.make_config(cfg, 17)
     K = C.shape[0]
-    if path == 2 and K > 4096:
+    if path == 2 and K > 16384:
         pytest.skip("K over the bucket path's limit (covered by the sort path)")
     lab = noisy_labels(meta["generating_centre"], K, cfg)
     st = check(X, lab, C, run_update(X, lab, C, path=path))

@@ -138,6 +138,21 @@ void upd_hist_kernel(const int32_t *__restrict__ keys_in, int N, int K, int shif
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: shifts right by
+// 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside
+// the row read 0), then each row adds the last lane of the rows before it
+// (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 1, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 2, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 4, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 8, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowBcast15, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowBcast31, 0xc, 0xf, false);
+    return x;
+}
+
 // Exclusive scan of h[0..M) in place (M a multiple of 4), one workgroup:
 // each thread owns a contiguous run of 16-byte groups, loaded eight at a
 // time into registers so the loads overlap (one batch when M <= 32768, and
@@ -165,26 +180,14 @@ void upd_scan_kernel(int32_t *__restrict__ h, int M) {
         for (int u = 0; u < kBatch; ++u)
             sum += keep[u][0] + keep[u][1] + keep[u][2] + keep[u][3];
     }
-    // Block-wide exclusive prefix of the per-thread sums: within each wave by
-    // shuffles, then across the 16 wave totals.
-    int x = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off)
-            x += y;
-    }
+    // Block-wide exclusive prefix of the per-thread sums: within each wave,
+    // then across the 16 wave totals.
+    const int x = wave_inclusive_sum(sum);
     if (lane == 63)
         wtot[w] = x;
     __syncthreads();
     if (w == 0) {
-        int t = lane < kScanThreads / 64 ? wtot[lane] : 0;
-#pragma unroll
-        for (int off = 1; off < kScanThreads / 64; off <<= 1) {
-            const int y = __shfl_up(t, off);
-            if (lane >= off)
-                t += y;
-        }
+        const int t = wave_inclusive_sum(lane < kScanThreads / 64 ? wtot[lane] : 0);
         if (lane < kScanThreads / 64)     // same wave: its reads came first
             wtot[lane] = t;
     }
@@ -798,6 +801,7 @@ constexpr int kSlotIdxBits = 24;     // a slot word: point index | cluster in bu
 static_assert(kMaxBinPoints <= (int64_t(1) << kSlotIdxBits), "point indices fit the slot word");
 static_assert(kSlotIdxBits + kMaxBucketLog2 <= 31, "the cluster in its bucket fits the slot word");
 
+
 // Tile t: positions [t << tl, min(N, (t + 1) << tl)).  Wave w owns the
 // contiguous eighth [w q, (w + 1) q) of the tile (q = 2^tl / 8), so the
 // stable order is: bucket, then wave, then position inside the wave.
@@ -892,13 +896,7 @@ void upd_bin_kernel(const int32_t *__restrict__ labels, int N, int K, int s_log2
                 sum += tot[j];
             }
         }
-        int x = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off);
-            if (lane >= off)
-                x += y;
-        }
+        const int x = wave_inclusive_sum(sum);
         if (lane == 63)
             wtot[w] = x;
         __syncthreads();
@@ -1043,16 +1041,7 @@ __device__ __forceinline__ SlotWords gather_slot_words(const int32_t *__restrict
             wv[p] = sidx[p < sum ? word_pos(p) : stand_in];
     }
     const int sum = seg[0] + seg[1];
-    int x[kTilesPerThread] = {seg[0], seg[1]};
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-        for (int u = 0; u < kTilesPerThread; ++u) {
-            const int y = __shfl_up(x[u], o);
-            if (lane >= o)
-                x[u] += y;
-        }
-    }
+    const int x[kTilesPerThread] = {wave_inclusive_sum(seg[0]), wave_inclusive_sum(seg[1])};
     if (lane == 63) {
         wtot[0][w] = x[0];
         wtot[1][w] = x[1];
@@ -1387,13 +1376,7 @@ void upd_bucket_runs_kernel(const uint16_t *__restrict__ X, const int32_t *__res
             if (lane < S)
                 for (int g = 0; g < ng; ++g)
                     t += grp[g][lane];
-            int x = t;
-#pragma unroll
-            for (int o = 1; o < S; o <<= 1) {
-                const int y = __shfl_up(x, o);
-                if (lane >= o)
-                    x += y;
-            }
+            const int x = wave_inclusive_sum(t);
             if (lane < S) {
                 int st = x - t;
                 for (int g = 0; g < ng; ++g) {

@@ -79,6 +79,8 @@ SMALL = [  # (N, D, K): ragged everywhere, K > N, 1, 2 and 3 radix passes,
     (5000, 192, 70000), (20000, 96, 255), (20000, 112, 256),
     (9000, 64, 5000), (7000, 256, 9000), (6000, 512, 16384), (30000, 128, 12289),
     (9000, 64, 4095), (7000, 256, 3073),
+    # buckets of 8 and 16 clusters (sorted by cluster in LDS) at odd D
+    (5000, 80, 8000), (3000, 48, 16384), (4000, 192, 6000), (6000, 112, 12000),
 ]
 
 
@@ -160,6 +162,26 @@ def test_skewed_and_chunk_aligned_clusters(path):
     out = run_update(X, lab, C, path=path)
     check(X, lab, C, out)
     assert out["counts"][8] == 0 and out["counts"][5] > 30000
+
+
+@PATHS
+def test_large_bucket_of_sixteen_clusters(path):
+    """K = 16384 (buckets of 16 clusters) with bucket 0 holding over 2048
+    points (three large clusters): it is sorted and summed 512 slots at a
+    time and its clusters' runs cross chunk edges and wave quarters; the
+    other buckets fit LDS whole."""
+    N, D, K = 40000, 64, 16384
+    X, C, a = W.gaussian_mixture(N, D, K, 79)
+    lab = noisy_labels(a, K, 79)
+    rng = np.random.default_rng(80)
+    idx = rng.permutation(N)
+    lab[idx[:5000]] = 5                                  # bucket 0: clusters 0..15
+    lab[idx[5000:5000 + 512 - 1]] = 6
+    lab[idx[5511:5511 + 300]] = 15
+    assert (lab[(lab >= 0) & (lab < 16)].size) > 2048
+    out = run_update(X, lab, C, path=path)
+    st = check(X, lab, C, out)
+    assert st["clusters"] == K and out["counts"][5] >= 5000
 
 
 @PATHS

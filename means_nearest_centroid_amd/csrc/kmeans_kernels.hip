@@ -815,11 +815,30 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 
     // Block b lives in stage cc/nc, block b+1 in cn/nn; block b+2 is fetched
     // into cc/nc once the barrier shows nobody reads block b any more.
+    // Alternating wave priority pays where blocks hold eight tiles; at D =
+    // 256 (two tiles per block) it measured 0.7% slower, and with four-wave
+    // workgroups the waves sharing a SIMD belong to different workgroups.
+    constexpr bool kAlternatePriority = WAVES == 8 && TB == 8;
     auto do_block = [&](int b, uint8_t *cc, float *nc, uint8_t *cn, float *nn) KM_INLINE {
         const int kb = k_begin + b * BK;
         const bool share = b % SHARE_BLOCKS == 0;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
+            // Waves w and w + 4 of an eight-wave workgroup share a SIMD, and
+            // when both can issue the older one goes first: it reaches the
+            // block's barrier early and waits there (29% of the K loop for
+            // waves 0-3 against 2% for waves 4-7, D = 128) while its partner
+            // runs alone.  Giving each wave of the pair the higher priority
+            // for alternate pairs of tiles keeps them level (10% and 2% with
+            // a switch every tile; every two tiles measured 0.3-0.5% faster
+            // than every tile or every four).
+            if constexpr (kAlternatePriority) {
+                if (wave < WAVES / 2) {
+                    if (j & 2) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
+                } else {
+                    if (j & 2) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+                }
+            }
             if (j + 1 < TB) {
                 tile(cc, nc, (j + 1) * kTileRows, kb + j * kTileRows, j, share);
             } else {
@@ -845,6 +864,8 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     if constexpr (NACC > 1)   // the last tile's last point block
         reduce(PB - 1, acc[PB > 1 ? PB - 1 : ((TB - 1) & 1)],
                k_begin + (nblocks - 1) * BK + (TB - 1) * kTileRows, false);
+    if constexpr (kAlternatePriority)
+        __builtin_amdgcn_s_setprio(0);
 
     // ---- merge the lanes that hold the same point ----
     int32_t lab[PB];

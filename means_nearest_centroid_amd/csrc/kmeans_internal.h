@@ -25,9 +25,9 @@ constexpr int32_t kNoLabel = 0x7fffffff;
 // (D <= 64) or two (D = 128) times as many workgroups when N is small.
 constexpr int wide_point_blocks(int ks) { return ks <= 4 ? 4 : (ks == 8 ? 2 : 1); }
 // Centroid rows per LDS block (one of two ring stages): whole 32-row tiles,
-// at most one norm per thread, about 32 KiB of centroid data (64 KiB at
-// D = 512, where one workgroup holds a CU).
-constexpr int k_block_rows(int ks) { return ks <= 4 ? 256 : (ks == 8 ? 256 : 64); }
+// at most one norm per thread; 64 KiB of centroid data at D = 128, 256 and
+// 512 (where one workgroup holds a CU), 32 KiB at D <= 64.
+constexpr int k_block_rows(int ks) { return ks <= 8 ? 256 : (ks == 16 ? 128 : 64); }
 // Waves per assign workgroup (two per SIMD when 8).
 constexpr int waves_per_wg(int ks) { return (ks == 8 || ks == 16) ? 8 : 4; }
 constexpr int points_per_wg(int ks, int pb) { return waves_per_wg(ks) * pb * kTileCols; }

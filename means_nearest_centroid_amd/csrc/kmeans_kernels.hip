@@ -536,8 +536,9 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     // offset): every fragment read is then one base register plus the tile's
     // row offset as the immediate.  Smaller stages need no such
     // registers; at D = 512 the 32 registers they take cost more than the
-    // adds they save (3% slower at 262144 x 512 x 4096; +0.9% at D = 128).
-    constexpr bool ST1_BASE = 2 * STAGE_BYTES > 65536 && MB * NKS <= 8;
+    // adds they save (3% slower at 262144 x 512 x 4096; +0.9% at D = 128,
+    // 8 registers, and part of the D = 256 gain below, 16 registers).
+    constexpr bool ST1_BASE = 2 * STAGE_BYTES > 65536 && MB * NKS <= 16;
     uint32_t a_off1[ST1_BASE ? MB : 1][ST1_BASE ? NKS : 1];
 #pragma unroll
     for (int m = 0; m < (ST1_BASE ? MB : 0); ++m)
@@ -815,10 +816,12 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
 
     // Block b lives in stage cc/nc, block b+1 in cn/nn; block b+2 is fetched
     // into cc/nc once the barrier shows nobody reads block b any more.
-    // Alternating wave priority pays where blocks hold eight tiles; at D =
-    // 256 (two tiles per block) it measured 0.7% slower, and with four-wave
-    // workgroups the waves sharing a SIMD belong to different workgroups.
-    constexpr bool kAlternatePriority = WAVES == 8 && TB == 8;
+    // Alternating wave priority pays where blocks hold eight tiles (D = 128)
+    // or four (D = 256: with 128-row blocks and the stage-1 base registers,
+    // 2.4-3.0% faster than 64-row blocks without them; with two tiles per
+    // block it measured 0.7% slower).  With four-wave workgroups the waves
+    // sharing a SIMD belong to different workgroups.
+    constexpr bool kAlternatePriority = WAVES == 8 && (TB == 8 || TB == 4);
     auto do_block = [&](int b, uint8_t *cc, float *nc, uint8_t *cn, float *nn) KM_INLINE {
         const int kb = k_begin + b * BK;
         const bool share = b % SHARE_BLOCKS == 0;

@@ -142,7 +142,7 @@ def test_plan_for_the_workloads(lib):
         assert plans[i]["path"] == km.PATH_DIRECT and plans[i]["splits"] == 1
     assert plans[3]["points_per_wg"] == 512 and plans[4]["points_per_wg"] == 256
     for i in (1, 2):       # small N: narrow tiles (one 32-point block per wave)
-        assert plans[i]["path"] == km.PATH_DIRECT and plans[i]["points_per_wg"] == 128
+        assert plans[i]["path"] == km.PATH_DIRECT and plans[i]["points_per_wg"] == 256
     for i, c in CONFIGS.items():
         p = plans[i]
         assert p["padded_d"] >= c["D"] and p["padded_d"] % 16 == 0
@@ -154,8 +154,8 @@ def test_plan_for_the_workloads(lib):
 # points per workgroup): narrow tiles where N alone cannot fill the GPU and K
 # is at most 16 centroid blocks, the K-split above that, wide tiles at large N.
 SWEEP_PLANS = {
-    (65536, 64, 512): (1, 1, 128), (65536, 64, 4096): (1, 1, 128),
-    (65536, 64, 16384): (2, 4, 512), (65536, 128, 512): (1, 1, 256),
+    (65536, 64, 512): (1, 1, 256), (65536, 64, 4096): (1, 1, 256),
+    (65536, 64, 16384): (2, 4, 1024), (65536, 128, 512): (1, 1, 256),
     (65536, 128, 4096): (1, 1, 256), (262144, 128, 4096): (1, 1, 512),
     (262144, 128, 16384): (1, 1, 512), (1048576, 128, 4096): (1, 1, 512),
     (65536, 256, 512): (1, 1, 256), (65536, 256, 4096): (1, 1, 256),
@@ -178,8 +178,8 @@ def test_plan_follows_the_compute_unit_count(lib):
     assert km.kmeans_plan(65536, 128, 16384, 128)["path"] == km.PATH_DIRECT
     assert km.kmeans_plan(65536, 128, 16384, 1024)["splits"] == 8   # one full round
     # narrow tiles only when they fit in one round
-    assert km.kmeans_plan(65536, 64, 4096, 256)["points_per_wg"] == 128
-    assert km.kmeans_plan(65536, 64, 4096, 64)["points_per_wg"] == 512
+    assert km.kmeans_plan(65536, 64, 4096, 256)["points_per_wg"] == 256
+    assert km.kmeans_plan(65536, 64, 4096, 64)["points_per_wg"] == 1024
 
 
 @pytest.mark.parametrize("N,D,K", [(1, 16, 1), (100, 80, 7), (5000, 192, 3000),

@@ -365,8 +365,8 @@ def test_wave_tail_launch_equals_wide_bitwise(N, D, K):
     tiles on offset pointers; outputs must be bitwise those of one wide
     launch, and correct around the boundary between the two launches."""
     plan = km.kmeans_plan(N, D, K)
-    wide = 512
-    head = (N // wide // 256) * 256 * wide if D == 128 else (N // wide // 512) * 512 * wide
+    wide = 512 if D == 128 else 1024                # points of a wide workgroup
+    head = (N // wide // 256) * 256 * wide          # whole rounds: one per CU, 256 CUs
     assert plan["workgroups"] > head // wide        # a tail launch is planned
     X, C, _ = W.gaussian_mixture(N, D, K, 130 + D)
     la, ma = run(X, C)

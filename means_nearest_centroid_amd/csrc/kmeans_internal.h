@@ -29,7 +29,7 @@ constexpr int wide_point_blocks(int ks) { return ks <= 4 ? 4 : (ks == 8 ? 2 : 1)
 // 512 (where one workgroup holds a CU), 32 KiB at D <= 64.
 constexpr int k_block_rows(int ks) { return ks <= 8 ? 256 : (ks == 16 ? 128 : 64); }
 // Waves per assign workgroup (two per SIMD when 8).
-constexpr int waves_per_wg(int ks) { return (ks == 4 || ks == 8 || ks == 16) ? 8 : 4; }
+constexpr int waves_per_wg(int ks) { return ks <= 16 ? 8 : 4; }
 constexpr int points_per_wg(int ks, int pb) { return waves_per_wg(ks) * pb * kTileCols; }
 // Waves per SIMD the kernel's register budget is sized for.
 constexpr int waves_per_simd(int ks) { return ks >= 32 ? 1 : 2; }

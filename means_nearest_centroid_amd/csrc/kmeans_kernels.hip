@@ -398,8 +398,8 @@ __device__ __forceinline__ int lowest_row_of_min_32x32_chain(const f32x16 &s, fl
     return row;
 }
 
-// One workgroup = WAVES waves (8 at D = 64 to 256, so that one centroid
-// stream per CU feeds two waves per SIMD; 4 at D <= 32 and 512); wave w owns P blocks of
+// One workgroup = WAVES waves (8 up to D = 256, so that one centroid stream
+// per CU feeds two waves per SIMD; 4 at D = 512, one wave per SIMD); wave w owns P blocks of
 // 32 points.  Grid: x = point workgroups, y = K-ranges of k_chunk centroids.
 //
 // Data movement.  Centroid rows stream through two LDS stages in blocks of

@@ -78,8 +78,17 @@ def traffic_record(config: int, kind: str = "assign"):
     return rec
 
 
+# Record kind of the assign launch's traffic: the automatic dispatch's, or a
+# forced path's ("assign_persistent" for the queue kernel).
+ASSIGN_PATH_NAMES = {0: "automatic", 1: "direct", 2: "split", 3: "persistent"}
+
+
+def assign_traffic_kind(assign_path: int) -> str:
+    return "assign" if assign_path == 0 else f"assign_{ASSIGN_PATH_NAMES[assign_path]}"
+
+
 def _kernel_kind(name: str):
-    if "assign_kernel" in name:
+    if "assign_kernel" in name or "assign_queue_kernel" in name:
         return "assign"
     if "merge_kernel" in name:
         return "merge"
@@ -580,6 +589,12 @@ def main():
     ap.add_argument("--record-command", default="", help="command stored with the record")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the MFMA-only probe (mfma_ceiling: null)")
+    ap.add_argument("--assign-path", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="0 the automatic dispatch (the headline figure); 1 direct, 2 split, "
+                         "3 persistent (the work-queue kernel), forced through "
+                         "kmeans_assign_path")
+    ap.add_argument("--assign-count", type=int, default=0,
+                    help="with --assign-path: its count argument (0 automatic)")
     ap.add_argument("--update-path", type=int, default=0, choices=(0, 1, 2),
                     help="with --update: 0 automatic, 1 the radix-sort path, 2 the bucket path")
     ap.add_argument("--update", action="store_true",
@@ -593,7 +608,7 @@ def main():
     if args.record_traffic:
         record_traffic(args.config, args.record_traffic[0], args.record_traffic[1],
                        args.copy_calibration_mib or 256, args.record_command,
-                       kind="update" if args.update else "assign")
+                       kind="update" if args.update else assign_traffic_kind(args.assign_path))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -640,7 +655,11 @@ def main():
     def assign_only(i):
         j = i % len(sets)
         X, C = sets[j]
-        km.kmeans_assign(X, C, norms[j], labels[j], min_dist[j], stream=stream)
+        if args.assign_path == 0:
+            km.kmeans_assign(X, C, norms[j], labels[j], min_dist[j], stream=stream)
+        else:
+            km.kmeans_assign_path(X, C, norms[j], args.assign_path, args.assign_count,
+                                  labels[j], min_dist[j], stream=stream)
 
     def step(i):
         norms_only(i)
@@ -703,12 +722,20 @@ def main():
     flops = 2.0 * N * D * K
     avg_assign_s = assign_ms / 1e3
     achieved = flops / avg_assign_s / 1e12
-    traffic = traffic_record(args.config)
+    traffic = traffic_record(args.config, assign_traffic_kind(args.assign_path))
+    if args.assign_path == 0:
+        kernel = ("kmeans_assign (assign_kernel"
+                  + (" + merge_kernel" if plan["path"] == km.PATH_SPLIT else "") + ")")
+        path_name = "split" if plan["path"] == km.PATH_SPLIT else "direct"
+    else:
+        kernel = (f"kmeans_assign_path, {ASSIGN_PATH_NAMES[args.assign_path]} forced ("
+                  + {1: "assign_kernel", 2: "assign_kernel + merge_kernel",
+                     3: "assign_queue_kernel"}[args.assign_path] + ")")
+        path_name = f"{ASSIGN_PATH_NAMES[args.assign_path]} (forced, count {args.assign_count})"
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_DENSE_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / BF16_DENSE_PEAK_TFLOPS, 4),
                     traffic=(traffic["hbm_bytes_per_launch"] if traffic else None),
-                    kernel="kmeans_assign (assign_kernel"
-                           + (" + merge_kernel" if plan["path"] == km.PATH_SPLIT else "") + ")",
+                    kernel=kernel,
                     avg_launch_us=round(avg_assign_s * 1e6, 2),
                     flop_per_launch=flops)
 
@@ -760,7 +787,7 @@ def main():
         "config": {
             "workload": f"kmeans assignment, {cfg['name']}, bf16 Gaussian mixture, "
                         f"seeds {list(W.SEEDS)} rotated",
-            "N": N, "D": D, "K": K, "path": "split" if plan["path"] == 2 else "direct",
+            "N": N, "D": D, "K": K, "path": path_name,
             "splits": plan["splits"], "settle_ms": args.settle_ms, "settle_steps": settled,
         },
         "roofline": roofline,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KMEANS_ABI_VERSION 6
+#define KMEANS_ABI_VERSION 7
 
 /* Supported feature dimension: 16 <= D <= 512 and D % 16 == 0. */
 #define KMEANS_MIN_D 16
@@ -64,7 +64,9 @@ typedef enum {
 typedef enum {
     KMEANS_PATH_AUTO = 0,    /* shape-based choice (what kmeans_assign does) */
     KMEANS_PATH_DIRECT = 1,  /* one pass: every workgroup scans all K centroids */
-    KMEANS_PATH_SPLIT = 2    /* K split over `count` ranges + a merge pass */
+    KMEANS_PATH_SPLIT = 2,   /* K split over `count` ranges + a merge pass */
+    KMEANS_PATH_PERSISTENT = 3  /* direct, one round of workgroups taking point
+                                   tiles from a queue (kmeans_assign_path only) */
 } kmeans_path_t;
 
 /*
@@ -145,6 +147,18 @@ kmeans_status_t kmeans_assign_static(const void *X, const void *C, const float *
  *                           large N)
  *   KMEANS_PATH_SPLIT       number of K-ranges (clamped to 64 and to the
  *                           number of centroid blocks), wide tiles
+ *   KMEANS_PATH_PERSISTENT  number of workgroups (0: one per CU), wide
+ *                           tiles; each workgroup takes its first tile by
+ *                           its index and every later one from a queue of
+ *                           two counters that the library keeps per stream
+ *                           (created and zeroed on the stream's first such
+ *                           call, given back by kmeans_release_workspace),
+ *                           so workgroups on faster XCDs take more tiles
+ *                           instead of an equal share per XCD.  Centroids
+ *                           over 2 GiB: KMEANS_ERR_UNSUPPORTED, as for
+ *                           KMEANS_PATH_DIRECT.  Calls on one stream run in
+ *                           order and share its queue; another stream has
+ *                           its own.
  * Same arguments, outputs and errors as kmeans_assign (count < 0 is
  * KMEANS_ERR_INVALID_ARG); exists so that the paths can be compared bit for
  * bit and timed against each other (the pages' per-shape path table under
@@ -261,7 +275,8 @@ kmeans_status_t kmeans_update_path(const void *X, const int32_t *labels, const v
  * it before destroying a stream that was passed to those entry points (a new
  * stream could otherwise inherit the buffer while the old stream's calls
  * still run), or to give the memory back.  hipStreamPerThread gets one
- * buffer per calling thread (release it from that thread).  No-op when the
+ * buffer per calling thread (release it from that thread).  The same call
+ * gives back the stream's tile queue of the persistent path.  No-op when the
  * stream holds none; KMEANS_ERR_HIP if the free fails.
  */
 kmeans_status_t kmeans_release_workspace(hipStream_t stream);

@@ -35,6 +35,7 @@ KMEANS_ERR_NO_MEMORY = 5
 PATH_AUTO = 0
 PATH_DIRECT = 1
 PATH_SPLIT = 2
+PATH_PERSISTENT = 3
 # kmeans_update_path_t
 UPDATE_AUTO = 0
 UPDATE_SORT = 1
@@ -206,10 +207,11 @@ def kmeans_assign_static(X, C, norms, labels=None, min_dist=None, stream=None):
 
 def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, count: int = 0,
                        labels=None, min_dist=None, stream=None):
-    """``kmeans_assign`` with a forced path (``PATH_DIRECT`` or ``PATH_SPLIT``).
-    ``count``: for the split path the number of K-ranges (0: automatic); for
-    the direct path 1 selects narrow point tiles (32 points per wave), any
-    other value wide ones."""
+    """``kmeans_assign`` with a forced path (``PATH_DIRECT``, ``PATH_SPLIT`` or
+    ``PATH_PERSISTENT``).  ``count``: for the split path the number of
+    K-ranges (0: automatic); for the direct path 1 selects narrow point tiles
+    (32 points per wave), any other value wide ones; for the persistent path
+    the number of workgroups (0: one per CU)."""
     X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
     lib = load_library()
     _check(lib, lib.kmeans_assign_path(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
@@ -262,8 +264,9 @@ def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=N
 
 def kmeans_release_workspace(stream=None):
     """Return the stream's workspace (the K-split path's and the update's
-    scratch, kept between calls) to the device's memory pool, in stream
-    order; a later call on the stream allocates it again."""
+    scratch, kept between calls) and its tile queue (the persistent path's)
+    to the device's memory pool, in stream order; a later call on the stream
+    allocates them again."""
     lib = load_library()
     _check(lib, lib.kmeans_release_workspace(_stream_handle(stream)))
 

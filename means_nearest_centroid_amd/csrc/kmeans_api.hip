@@ -73,6 +73,11 @@ namespace {
 using WsKey = std::tuple<int, uintptr_t, size_t>;
 std::mutex g_ws_mutex;
 auto *g_ws = new std::map<WsKey, std::pair<void *, size_t>>();
+// The persistent path's tile queue per (device, stream, thread): two int32
+// counters in a small allocation of their own (the workspace above is
+// overwritten by other calls, the queue must stay zero between launches).
+auto *g_queues = new std::map<WsKey, int *>();
+constexpr size_t kQueueBytes = 256;
 constexpr size_t kWorkspaceGranule = size_t(1) << 20;
 
 WsKey ws_key(int dev, hipStream_t stream) {
@@ -112,13 +117,47 @@ WorkspaceLease::WorkspaceLease(hipStream_t stream, size_t bytes) {
 
 WorkspaceLease::~WorkspaceLease() { g_ws_mutex.unlock(); }
 
+QueueLease::QueueLease(hipStream_t stream) {
+    g_ws_mutex.lock();
+    int dev = 0;
+    error_ = hipGetDevice(&dev);
+    if (error_ != hipSuccess)
+        return;
+    int *&q = (*g_queues)[ws_key(dev, stream)];
+    if (q == nullptr) {
+        void *p = nullptr;
+        error_ = hipMallocAsync(&p, kQueueBytes, stream);
+        if (error_ == hipSuccess && p == nullptr)
+            error_ = hipErrorOutOfMemory;
+        if (error_ != hipSuccess)
+            return;
+        error_ = launch_zero_queue(static_cast<int *>(p), stream);
+        if (error_ != hipSuccess) {
+            (void)hipFreeAsync(p, stream);
+            return;
+        }
+        q = static_cast<int *>(p);
+    }
+    ptr_ = q;
+}
+
+QueueLease::~QueueLease() { g_ws_mutex.unlock(); }
+
 hipError_t release_workspace(hipStream_t stream) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return e;
-    auto it = g_ws->find(ws_key(dev, stream));
+    const WsKey key = ws_key(dev, stream);
+    auto qit = g_queues->find(key);
+    if (qit != g_queues->end()) {
+        int *q = qit->second;
+        g_queues->erase(qit);
+        if (q != nullptr && (e = hipFreeAsync(q, stream)) != hipSuccess)
+            return e;
+    }
+    auto it = g_ws->find(key);
     if (it == g_ws->end())
         return hipSuccess;
     void *p = it->second.first;
@@ -219,11 +258,12 @@ kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int
     kmeans_status_t st = check_shape(N, D, K);
     if (st != KMEANS_OK)
         return st;
-    if (path < KMEANS_PATH_AUTO || path > KMEANS_PATH_SPLIT)
+    if (path < KMEANS_PATH_AUTO || path > KMEANS_PATH_PERSISTENT)
         return fail(KMEANS_ERR_INVALID_ARG, "path=%d unknown", path);
     if (count < 0)
         return fail(KMEANS_ERR_INVALID_ARG, "count=%d must be >= 0", count);
-    if (kmeans::min_k_ranges(D, K) > 1 && path == KMEANS_PATH_DIRECT)
+    if (kmeans::min_k_ranges(D, K) > 1 &&
+        (path == KMEANS_PATH_DIRECT || path == KMEANS_PATH_PERSISTENT))
         return fail(KMEANS_ERR_UNSUPPORTED, "K=%lld rows of D=%lld: centroids over 2 GiB need "
                     "the split path", static_cast<long long>(K), static_cast<long long>(D));
     if (N == 0)
@@ -242,6 +282,16 @@ kmeans_status_t run_assign(const void *X, const void *C, const float *norms, int
     const auto *Cb = static_cast<const uint16_t *>(C);
     const int n = static_cast<int>(N), d = static_cast<int>(D), k = static_cast<int>(K);
 
+    if (pl.path == KMEANS_PATH_PERSISTENT) {
+        const kmeans::QueueLease queue(stream);
+        if (queue.error() != hipSuccess)
+            return fail(KMEANS_ERR_NO_MEMORY, "tile queue: %s", hipGetErrorString(queue.error()));
+        const hipError_t e = kmeans::launch_assign_queue(pl, Xb, Cb, norms, n, d, k, labels,
+                                                         min_dist, queue.ptr(), stream);
+        if (e != hipSuccess)
+            return fail(KMEANS_ERR_HIP, "assign launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
     if (pl.path == KMEANS_PATH_DIRECT) {
         const int head = n - pl.tail_points;
         hipError_t e = kmeans::launch_assign(pl, Xb, Cb, norms, head, d, k, labels, min_dist,

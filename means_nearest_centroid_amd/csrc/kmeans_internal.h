@@ -76,13 +76,13 @@ constexpr int mfma_geometry(int ks) { return ks == 8 || ks == 16 ? 16 : 32; }
 constexpr int64_t kG16MinWorkAtD64 = int64_t(1) << 28;
 
 struct Plan {
-    int path;          // 1 direct, 2 split (as kmeans_path_t)
+    int path;          // 1 direct, 2 split, 3 persistent (as kmeans_path_t)
     int geom;          // MFMA form: 16 (16x16x32) or 32 (32x32x16)
     int splits;        // K-ranges (grid.y)
     int ks;            // padded D / 16
     int pb;            // point blocks per wave (wide_point_blocks(ks) or 1)
     int tiles;         // point tiles of ppw points
-    int wgs;           // workgroups along N (grid.x)
+    int wgs;           // workgroups along N (grid.x; path 3: workgroups of the one round)
     int ppw;           // points per workgroup
     int bk;            // centroid rows per LDS block
     int k_chunk;       // centroids per K-range, multiple of bk
@@ -97,9 +97,9 @@ struct Plan {
 // rows (1 unless C is over 2 GiB); more than kMaxSplits is unsupported.
 int min_k_ranges(int64_t D, int64_t K);
 
-// force_path: 0 auto, 1 direct, 2 split; force_count: K-ranges (split) or
-// point blocks per wave (direct: 1 narrow, other wide), 0 auto;
-// compute_units: CUs of the GPU.
+// force_path: 0 auto, 1 direct, 2 split, 3 persistent; force_count: K-ranges
+// (split), point blocks per wave (direct: 1 narrow, other wide) or
+// workgroups (persistent), 0 auto; compute_units: CUs of the GPU.
 // Requires 1 <= N < 2^31, valid D, 1 <= K < 2^31 (checked by the caller).
 Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
                int compute_units);
@@ -138,6 +138,16 @@ hipError_t launch_assign(const Plan &plan, const uint16_t *X, const uint16_t *C,
                          const float *norms, int N, int D, int K, int32_t *labels,
                          float *min_dist, float *ws_score, int32_t *ws_label,
                          float *ws_xx, hipStream_t stream);
+
+// The persistent direct path (plan.path == 3): one round of plan.wgs
+// workgroups taking plan.tiles wide point tiles from `queue`, two int32
+// counters that are zero at launch and zero again at its end.  Launches that
+// share a queue must not overlap.
+hipError_t launch_assign_queue(const Plan &plan, const uint16_t *X, const uint16_t *C,
+                               const float *norms, int N, int D, int K, int32_t *labels,
+                               float *min_dist, int *queue, hipStream_t stream);
+// Zeroes a new queue's counters.
+hipError_t launch_zero_queue(int *queue, hipStream_t stream);
 
 hipError_t launch_merge(const Plan &plan, const uint16_t *X, const uint16_t *C,
                         const float *norms, int N, int D, int K, int32_t *labels,
@@ -181,7 +191,25 @@ private:
     hipError_t error_ = hipSuccess;
 };
 
-// Frees (stream-ordered) the current device's buffer kept for `stream`.
+// The persistent path's tile queue for `stream` (two int32 counters, zero
+// between launches), created and zeroed on first use; like WorkspaceLease it
+// holds the process-wide lock until destroyed.
+class QueueLease {
+public:
+    explicit QueueLease(hipStream_t stream);
+    ~QueueLease();
+    QueueLease(const QueueLease &) = delete;
+    QueueLease &operator=(const QueueLease &) = delete;
+    int *ptr() const { return ptr_; }
+    hipError_t error() const { return error_; }
+
+private:
+    int *ptr_ = nullptr;
+    hipError_t error_ = hipSuccess;
+};
+
+// Frees (stream-ordered) the current device's buffer and tile queue kept for
+// `stream`.
 hipError_t release_workspace(hipStream_t stream);
 
 }  // namespace kmeans

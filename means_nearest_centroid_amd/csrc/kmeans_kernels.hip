@@ -400,7 +400,10 @@ __device__ __forceinline__ int lowest_row_of_min_32x32_chain(const f32x16 &s, fl
 
 // One workgroup = WAVES waves (8 up to D = 256, so that one centroid stream
 // per CU feeds two waves per SIMD; 4 at D = 512, one wave per SIMD); wave w owns P blocks of
-// 32 points.  Grid: x = point workgroups, y = K-ranges of k_chunk centroids.
+// 32 points.  assign_tile is the whole computation for one point tile (the
+// workgroup's WAVES * P * 32 points) against one K-range; assign_kernel runs
+// it for tile x = blockIdx.x and K-range y = blockIdx.y, assign_queue_kernel
+// for a sequence of tiles taken from a queue.
 //
 // Data movement.  Centroid rows stream through two LDS stages in blocks of
 // BK rows.  Each block is copied global -> LDS by buffer_load ... lds (no
@@ -425,14 +428,12 @@ __device__ __forceinline__ int lowest_row_of_min_32x32_chain(const f32x16 &s, fl
 //       best = m, best_tile = tile, best_slot = slot
 // m is always one of its inputs, so the winner is exact; a strict '<' keeps
 // the earlier tile on equal scores, and the slot search keeps the lower row.
-template <int G, int KS, int P, int BK, int WAVES, int WPE>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
-                          amdgpu_waves_per_eu(WPE, WPE)))
-void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
-                   const float *__restrict__ norms, int N, int D, int K, int k_chunk,
-                   int write_partials, int x_stream, int32_t *__restrict__ labels,
-                   float *__restrict__ min_dist, float *__restrict__ ws_score,
-                   int32_t *__restrict__ ws_label, float *__restrict__ ws_xx) {
+template <int G, int KS, int P, int BK, int WAVES>
+__device__ KM_INLINE inline void assign_tile(
+    int tile_x, int tid, const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
+    const float *__restrict__ norms, int N, int D, int K, int k_chunk, int write_partials,
+    int x_stream, int32_t *__restrict__ labels, float *__restrict__ min_dist,
+    float *__restrict__ ws_score, int32_t *__restrict__ ws_label, float *__restrict__ ws_xx) {
     // MFMA geometry.  G = 32: v_mfma_f32_32x32x16_bf16, one 32-row A block
     // per tile, 32-point B blocks, k-steps of 16; lane = (pcol = lane % 32,
     // kq = lane / 32); accumulator element e is tile row 8(e/4) + 4kq + e%4.
@@ -466,7 +467,6 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     __shared__ __attribute__((aligned(16))) float n_st0[BK];
     __shared__ __attribute__((aligned(16))) float n_st1[BK];
 
-    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int pcol = lane % G;   // point column of a B block; row of an A block
@@ -475,7 +475,7 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     const int split = blockIdx.y;
     const int k_begin = split * k_chunk;
     const int k_rows = min(K, k_begin + k_chunk) - k_begin;
-    const int wg_point0 = blockIdx.x * (WAVES * P * kTileCols);
+    const int wg_point0 = tile_x * (WAVES * P * kTileCols);
     const int wg_points = min(N - wg_point0, WAVES * P * kTileCols);
     const uint32_t row_bytes = static_cast<uint32_t>(D) * 2u;
 
@@ -964,6 +964,79 @@ void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ 
     }
 }
 
+template <int G, int KS, int P, int BK, int WAVES, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void assign_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
+                   const float *__restrict__ norms, int N, int D, int K, int k_chunk,
+                   int write_partials, int x_stream, int32_t *__restrict__ labels,
+                   float *__restrict__ min_dist, float *__restrict__ ws_score,
+                   int32_t *__restrict__ ws_label, float *__restrict__ ws_xx) {
+    assign_tile<G, KS, P, BK, WAVES>(blockIdx.x, threadIdx.x, X, C, norms, N, D, K, k_chunk,
+                                     write_partials, x_stream, labels, min_dist, ws_score,
+                                     ws_label, ws_xx);
+}
+
+// Persistent form of the direct path: one round of workgroups that take point
+// tiles from a queue until none is left.  A workgroup's first tile is its
+// blockIdx.x; every later one is a ticket from queue[0] (an atomic add) plus
+// gridDim.x.  The hardware hands workgroups to the eight XCDs in turn, an
+// equal share each, whatever their clocks; with the queue a workgroup on a
+// faster XCD simply takes more tiles.  Each tile is assign_tile, so every
+// point's outputs are bitwise those of assign_kernel.  The queue counters
+// (queue[0], queue[1]) must be zero at launch and are zero again when the
+// launch ends: a workgroup that draws a ticket past the last tile counts
+// itself out in queue[1], and the last one out resets both.  Launches that
+// share a queue must not overlap (the caller keeps one queue per stream).
+template <int G, int KS, int P, int BK, int WAVES, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void assign_queue_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ C,
+                         const float *__restrict__ norms, int N, int D, int K, int k_chunk,
+                         int x_stream, int tiles, int32_t *__restrict__ labels,
+                         float *__restrict__ min_dist, int *__restrict__ queue) {
+    __shared__ int next_tile;
+    int t = blockIdx.x;
+    while (t < tiles) {
+        // The thread index, opaque on every tile: otherwise the compiler
+        // hoists the per-lane offsets of the tile's prologue and epilogue out
+        // of this loop and holds them through the K loop, where the
+        // registers are all taken.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        assign_tile<G, KS, P, BK, WAVES>(t, tid, X, C, norms, N, D, K, k_chunk, 0, x_stream,
+                                         labels, min_dist, nullptr, nullptr, nullptr);
+        // Every wave is done with the tile's LDS stages and with the last
+        // ticket before the next one is drawn and the stages refilled.  (A
+        // ticket drawn earlier, when the tile's last centroid block starts,
+        // measured 1.5-3% slower: it reserves a tile ahead and so gives up
+        // most of the balancing.)
+        __syncthreads();
+        if (tid == 0)
+            next_tile = __hip_atomic_fetch_add(&queue[0], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) + static_cast<int>(gridDim.x);
+        __syncthreads();
+        t = next_tile;
+    }
+    if (threadIdx.x == 0) {
+        // Release: this workgroup's last ticket precedes its count; the
+        // workgroup that brings the count to gridDim.x sees every ticket
+        // drawn and leaves both counters at zero for the next launch.
+        const int out = __hip_atomic_fetch_add(&queue[1], 1, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (out == static_cast<int>(gridDim.x) - 1) {
+            __hip_atomic_store(&queue[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&queue[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Zeroes a queue's two counters (once, when the queue is created).
+__global__ void zero_queue_kernel(int *queue) {
+    if (threadIdx.x < 2)
+        queue[threadIdx.x] = 0;
+}
+
 // Second pass of the K-split path: (score, index) minimum over the splits,
 // then the winner's squared distance summed in the order the assign kernel
 // uses for the geometry G of this D (lane q of a point adds its 8-wide
@@ -1031,13 +1104,24 @@ template <int KS, int G, int P>
 hipError_t launch_assign_kp(const Plan &pl, const uint16_t *X, const uint16_t *C,
                             const float *norms, int N, int D, int K, int32_t *labels,
                             float *min_dist, float *ws_score, int32_t *ws_label,
-                            float *ws_xx, hipStream_t stream) {
+                            float *ws_xx, int *queue, hipStream_t stream) {
     constexpr int BK = k_block_rows(KS);
     constexpr int WAVES = waves_per_wg(KS);
     constexpr int WPE = waves_per_simd(KS);
     static_assert(assign_wgs_per_cu(KS) >= 1, "workgroup must fit a CU");
     const int partial = ws_score != nullptr ? 1 : 0;
     const int x_stream = static_cast<int64_t>(N) * D * 2 > kStreamPointBytes ? 1 : 0;
+    if (queue != nullptr) {
+        // The queue path takes wide tiles only (make_plan); not instantiated
+        // for narrow ones.
+        if constexpr (P == wide_point_blocks(KS)) {
+            hipLaunchKernelGGL((assign_queue_kernel<G, KS, P, BK, WAVES, WPE>), dim3(pl.wgs),
+                               dim3(64 * WAVES), 0, stream, X, C, norms, N, D, K, pl.k_chunk,
+                               x_stream, pl.tiles, labels, min_dist, queue);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL((assign_kernel<G, KS, P, BK, WAVES, WPE>), dim3(pl.wgs, pl.splits), dim3(64 * WAVES),
                        0, stream, X, C, norms, N, D, K, pl.k_chunk, partial, x_stream, labels,
                        min_dist, ws_score, ws_label, ws_xx);
@@ -1048,27 +1132,27 @@ template <int KS, int G>
 hipError_t launch_assign_kg(const Plan &pl, const uint16_t *X, const uint16_t *C,
                             const float *norms, int N, int D, int K, int32_t *labels,
                             float *min_dist, float *ws_score, int32_t *ws_label,
-                            float *ws_xx, hipStream_t stream) {
+                            float *ws_xx, int *queue, hipStream_t stream) {
     constexpr int WIDE = wide_point_blocks(KS);
     if (WIDE > 1 && pl.pb == 1)
         return launch_assign_kp<KS, G, 1>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
-                                          ws_label, ws_xx, stream);
+                                          ws_label, ws_xx, queue, stream);
     return launch_assign_kp<KS, G, WIDE>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score,
-                                         ws_label, ws_xx, stream);
+                                         ws_label, ws_xx, queue, stream);
 }
 
 template <int KS>
 hipError_t launch_assign_ks(const Plan &pl, const uint16_t *X, const uint16_t *C,
                             const float *norms, int N, int D, int K, int32_t *labels,
                             float *min_dist, float *ws_score, int32_t *ws_label,
-                            float *ws_xx, hipStream_t stream) {
+                            float *ws_xx, int *queue, hipStream_t stream) {
     if constexpr (KS == 4) {
         if (pl.geom == 16)
             return launch_assign_kg<KS, 16>(pl, X, C, norms, N, D, K, labels, min_dist,
-                                            ws_score, ws_label, ws_xx, stream);
+                                            ws_score, ws_label, ws_xx, queue, stream);
     }
     return launch_assign_kg<KS, mfma_geometry(KS)>(pl, X, C, norms, N, D, K, labels, min_dist,
-                                                   ws_score, ws_label, ws_xx, stream);
+                                                   ws_score, ws_label, ws_xx, queue, stream);
 }
 
 }  // namespace
@@ -1079,19 +1163,41 @@ hipError_t launch_norms(const uint16_t *C, int K, int D, float *norms, hipStream
     return hipGetLastError();
 }
 
+namespace {
+hipError_t launch_assign_any(const Plan &pl, const uint16_t *X, const uint16_t *C,
+                             const float *norms, int N, int D, int K, int32_t *labels,
+                             float *min_dist, float *ws_score, int32_t *ws_label,
+                             float *ws_xx, int *queue, hipStream_t stream) {
+    switch (pl.ks) {
+    case 1: return launch_assign_ks<1>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, queue, stream);
+    case 2: return launch_assign_ks<2>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, queue, stream);
+    case 4: return launch_assign_ks<4>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, queue, stream);
+    case 8: return launch_assign_ks<8>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, queue, stream);
+    case 16: return launch_assign_ks<16>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, queue, stream);
+    case 32: return launch_assign_ks<32>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, queue, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace
+
 hipError_t launch_assign(const Plan &pl, const uint16_t *X, const uint16_t *C,
                          const float *norms, int N, int D, int K, int32_t *labels,
                          float *min_dist, float *ws_score, int32_t *ws_label,
                          float *ws_xx, hipStream_t stream) {
-    switch (pl.ks) {
-    case 1: return launch_assign_ks<1>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, stream);
-    case 2: return launch_assign_ks<2>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, stream);
-    case 4: return launch_assign_ks<4>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, stream);
-    case 8: return launch_assign_ks<8>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, stream);
-    case 16: return launch_assign_ks<16>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, stream);
-    case 32: return launch_assign_ks<32>(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label, ws_xx, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_assign_any(pl, X, C, norms, N, D, K, labels, min_dist, ws_score, ws_label,
+                             ws_xx, nullptr, stream);
+}
+
+hipError_t launch_assign_queue(const Plan &pl, const uint16_t *X, const uint16_t *C,
+                               const float *norms, int N, int D, int K, int32_t *labels,
+                               float *min_dist, int *queue, hipStream_t stream) {
+    return launch_assign_any(pl, X, C, norms, N, D, K, labels, min_dist, nullptr, nullptr,
+                             nullptr, queue, stream);
+}
+
+hipError_t launch_zero_queue(int *queue, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_queue_kernel, dim3(1), dim3(64), 0, stream, queue);
+    return hipGetLastError();
 }
 
 hipError_t launch_merge(const Plan &pl, const uint16_t *X, const uint16_t *C,
@@ -1199,6 +1305,14 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
     if (pl.path == 1) {
         pl.splits = 1;
         pl.k_chunk = nkb * pl.bk;
+    }
+    if (force_path == 3 && pl.path == 1) {
+        // Persistent: wide tiles, one round of workgroups (one per CU unless
+        // force_count names another count), never more than the tiles.
+        pl.path = 3;
+        const int round = force_count > 0 ? force_count : resident;
+        pl.wgs = round < pl.tiles ? round : pl.tiles;
+        return pl;
     }
 
     // Wave tail: wide tiles that fill only part of their last round (at most

@@ -199,9 +199,9 @@ def test_centroids_over_2gib_are_split_or_refused(lib):
     p = km.kmeans_plan(64, 512, 2100000)
     assert p["path"] == km.PATH_SPLIT and p["splits"] >= 2
     assert km.kmeans_plan(64, 512, 2000000)["path"] == km.PATH_SPLIT   # small N anyway
-    st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 512, 2100000, FAKE, FAKE,
-                                km.PATH_DIRECT, 0, NUL)
-    assert st == km.KMEANS_ERR_UNSUPPORTED
+    for path in (km.PATH_DIRECT, km.PATH_PERSISTENT):
+        st = lib.kmeans_assign_path(FAKE, FAKE, FAKE, 10, 512, 2100000, FAKE, FAKE, path, 0, NUL)
+        assert st == km.KMEANS_ERR_UNSUPPORTED
     # Over 64 ranges of 2 GiB: unsupported on every path.
     with pytest.raises(km.KmeansError):
         km.kmeans_plan(64, 512, 200000000)

@@ -378,6 +378,50 @@ def test_wave_tail_launch_equals_wide_bitwise(N, D, K):
     parity.check(X, C, la, ma, idx=idx)
 
 
+@pytest.mark.parametrize("N,D,K,count", [
+    (5000, 64, 4096, 0),        # fewer tiles than CUs: one workgroup per tile
+    (300000, 128, 520, 0),      # 586 tiles over one workgroup per CU
+    (300000, 128, 520, 7),      # seven workgroups draw ~580 tickets
+    (100000, 16, 300, 3), (40000, 32, 257, 5), (70000, 256, 700, 0), (20000, 512, 300, 2),
+    (9000, 48, 129, 4), (1000, 80, 4000, 1),
+])
+def test_persistent_equals_direct_bitwise(N, D, K, count):
+    """The persistent path runs the same tiles as the direct path, in an order
+    set by a queue: every output must be bitwise the direct path's, on a first
+    and a second call (the queue must be back at zero after a launch)."""
+    X, C, _ = W.gaussian_mixture(N, D, K, 140 + D)
+    ld, md = run(X, C, km.PATH_DIRECT, 0)
+    for _ in range(2):
+        lp, mp = run(X, C, km.PATH_PERSISTENT, count)
+        assert np.array_equal(ld, lp)
+        assert md.tobytes() == mp.tobytes()
+    parity.check(X, C, lp, mp, idx=parity.sample_indices(N, 141, 256, 512, 64))
+
+
+def test_persistent_queue_per_stream_and_after_release():
+    """Each stream has its own queue; a released queue is made again, zeroed,
+    on the stream's next call."""
+    X, C, _ = W.gaussian_mixture(200000, 128, 300, 142)
+    ld, md = run(X, C, km.PATH_DIRECT, 0)
+    Xd, Cd = dev(X), dev(C)
+    n = km.kmeans_centroid_norms(Cd)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rnd in range(3):
+        for s in streams:
+            with torch.cuda.stream(s):
+                outs.append(km.kmeans_assign_path(Xd, Cd, n, km.PATH_PERSISTENT, 5))
+        if rnd == 1:
+            for s in streams:
+                with torch.cuda.stream(s):
+                    km.kmeans_release_workspace()
+    torch.cuda.synchronize()
+    for lab, mdist in outs:
+        assert np.array_equal(ld, lab.cpu().numpy())
+        assert md.tobytes() == mdist.cpu().numpy().tobytes()
+
+
 def test_deterministic_repeat():
     X, C, _ = W.make_config(2, 29)
     a = run(X, C)

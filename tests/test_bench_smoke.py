@@ -20,6 +20,21 @@ def test_multi_gpu_request_is_refused():
 
 
 @pytest.mark.gpu
+def test_bench_forced_persistent_path_checks_its_outputs():
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--config", "2",
+                        "--assign-path", "3", "--steps", "5", "--warmup", "2",
+                        "--settle-ms", "20", "--cpu-seconds", "0.2", "--no-ceiling"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["config"]["path"].startswith("persistent")
+    assert "assign_queue_kernel" in d["roofline"]["kernel"]
+    assert d["parity"]["bad"] == 0 and d["parity"]["points"] > 0
+
+
+@pytest.mark.gpu
 def test_bench_tiny_workload_emits_the_json_line():
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--config", "1",
                         "--steps", "5", "--warmup", "2", "--settle-ms", "20",

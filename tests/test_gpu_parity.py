@@ -166,6 +166,17 @@ def test_workload5_dyadic_ties_bit_exact(workload5):
     assert np.array_equal(md[idx].astype(np.float64), meta["dyadic_sqdist"])
 
 
+def test_workload5_persistent_and_split_bitwise(workload5):
+    """The adversarial set (non-finite slice, duplicates, equal rows, dyadic
+    ties) through the persistent and a K-split path: bitwise the direct
+    path's outputs."""
+    X, C, meta, lab, md = workload5
+    for path, count in ((km.PATH_PERSISTENT, 0), (km.PATH_PERSISTENT, 37), (km.PATH_SPLIT, 3)):
+        lp, mp = run(X, C, path, count)
+        assert np.array_equal(lab, lp), (path, count)
+        assert md.tobytes() == mp.tobytes(), (path, count)
+
+
 def test_workload5_duplicates_and_equal_rows(workload5):
     X, C, meta, lab, md = workload5
     for s, t in meta["dup_pairs"]:

@@ -243,7 +243,7 @@ def test_nonfinite_centroids():
     X[11, 4] = W.BF16_NINF
     X[12, 5] = W.BF16_QNAN
     for path, count in ((km.PATH_DIRECT, 0), (km.PATH_DIRECT, 1), (km.PATH_SPLIT, 0),
-                        (km.PATH_SPLIT, 3)):
+                        (km.PATH_SPLIT, 3), (km.PATH_PERSISTENT, 0)):
         lab, md = run(X, C, path, count)
         parity.check(X, C, lab, md)
 
@@ -260,9 +260,11 @@ def test_all_scores_infinite_or_nan():
     C[1, 1] = W.BF16_NINF             # row 1 with x_1 = 0: inf*0 -> NaN
     lab, md = run(x, C, km.PATH_DIRECT)
     lab2, md2 = run(x, C, km.PATH_SPLIT, 2)
+    lab3, md3 = run(x, C, km.PATH_PERSISTENT, 0)
     assert lab[0] == 2 and lab[1] == 2 and lab[2] == 0
     assert np.isinf(md[0]) and np.isnan(md[2])
-    assert np.array_equal(lab, lab2)
+    assert np.array_equal(lab, lab2) and np.array_equal(lab, lab3)
+    assert md.tobytes() == md3.tobytes()
     parity.check(x, C, lab, md)
 
 
@@ -546,7 +548,8 @@ def test_data_far_from_origin(offset, D):
     formed as ||x||^2 + score loses accuracy as the shift grows; the kernel
     sums (x - c)^2 directly past a ratio that depends on D, and min_dist must
     meet the acceptance rule on both sides of that switch (the small shifts
-    sit just below and just above it).  Split must equal direct bit for bit."""
+    sit just below and just above it).  Split and persistent must equal the
+    direct path bit for bit."""
     rng = np.random.default_rng(int(offset * 10) + D)
     N, K = 6000, 300
     mu = rng.standard_normal((K, D), dtype=np.float32)
@@ -558,5 +561,6 @@ def test_data_far_from_origin(offset, D):
     lab, md = run(X, C)
     st = parity.check(X, C, lab, md)
     assert st["bad_dist"] == 0
-    ls, ms = run(X, C, km.PATH_SPLIT, 3)
-    assert np.array_equal(lab, ls) and md.tobytes() == ms.tobytes()
+    for path, count in ((km.PATH_SPLIT, 3), (km.PATH_PERSISTENT, 2)):
+        ls, ms = run(X, C, path, count)
+        assert np.array_equal(lab, ls) and md.tobytes() == ms.tobytes(), (path, count)

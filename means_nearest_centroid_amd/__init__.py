@@ -103,11 +103,19 @@ def _check(lib, status: int):
         raise KmeansError(status, lib.kmeans_last_error().decode(errors="replace"))
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device=None):
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif device is not None and stream.device != device:
+        raise ValueError(f"stream is on {stream.device} but the tensors on {device}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(device):
+    """The library launches on the current HIP device: make it the tensors'."""
+    import torch
+    return torch.cuda.device(device)
 
 
 def _ptr(t):
@@ -161,7 +169,9 @@ def kmeans_centroid_norms(C, norms=None, stream=None):
         norms = torch.empty(K, dtype=torch.float32, device=C.device)
     _vector(norms, "norms", torch.float32, K, C.device)
     lib = load_library()
-    _check(lib, lib.kmeans_centroid_norms(_ptr(C), K, D, _ptr(norms), _stream_handle(stream)))
+    with _on(C.device):
+        _check(lib, lib.kmeans_centroid_norms(_ptr(C), K, D, _ptr(norms),
+                                              _stream_handle(stream, C.device)))
     return norms
 
 
@@ -189,8 +199,9 @@ def kmeans_assign(X, C, norms, labels=None, min_dist=None, stream=None):
     """Nearest centroid per point: ``(labels int32 [N], min_dist fp32 [N])``."""
     X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
     lib = load_library()
-    _check(lib, lib.kmeans_assign(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
-                                  _ptr(min_dist), _stream_handle(stream)))
+    with _on(X.device):
+        _check(lib, lib.kmeans_assign(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
+                                      _ptr(min_dist), _stream_handle(stream, X.device)))
     return labels, min_dist
 
 
@@ -200,8 +211,10 @@ def kmeans_assign_static(X, C, norms, labels=None, min_dist=None, stream=None):
     to allocate nothing at all).  Calls that overlap on one GPU race."""
     X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
     lib = load_library()
-    _check(lib, lib.kmeans_assign_static(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
-                                         _ptr(min_dist), _stream_handle(stream)))
+    with _on(X.device):
+        _check(lib, lib.kmeans_assign_static(_ptr(X), _ptr(C), _ptr(norms), N, D, K,
+                                             _ptr(labels), _ptr(min_dist),
+                                             _stream_handle(stream, X.device)))
     return labels, min_dist
 
 
@@ -214,8 +227,10 @@ def kmeans_assign_path(X, C, norms, path: int = PATH_AUTO, count: int = 0,
     the number of workgroups (0: one per CU)."""
     X, C, norms, N, D, K, labels, min_dist = _assign_args(X, C, norms, labels, min_dist)
     lib = load_library()
-    _check(lib, lib.kmeans_assign_path(_ptr(X), _ptr(C), _ptr(norms), N, D, K, _ptr(labels),
-                                       _ptr(min_dist), path, count, _stream_handle(stream)))
+    with _on(X.device):
+        _check(lib, lib.kmeans_assign_path(_ptr(X), _ptr(C), _ptr(norms), N, D, K,
+                                           _ptr(labels), _ptr(min_dist), path, count,
+                                           _stream_handle(stream, X.device)))
     return labels, min_dist
 
 
@@ -256,9 +271,10 @@ def kmeans_update(X, labels, C_old, C_new=None, norms=None, counts=None, means=N
         if t is not None:
             _vector(t, name, dt, n, dev)
     lib = load_library()
-    _check(lib, lib.kmeans_update_path(_ptr(X), _ptr(labels), _ptr(C_old), N, D, K,
-                                       _ptr(C_new), _ptr(norms), _ptr(counts), _ptr(means),
-                                       int(path), _stream_handle(stream)))
+    with _on(dev):
+        _check(lib, lib.kmeans_update_path(_ptr(X), _ptr(labels), _ptr(C_old), N, D, K,
+                                           _ptr(C_new), _ptr(norms), _ptr(counts), _ptr(means),
+                                           int(path), _stream_handle(stream, dev)))
     return C_new, norms, counts, means
 
 

@@ -1256,40 +1256,54 @@ Plan make_plan(int64_t N, int64_t D, int64_t K, int force_path, int force_count,
         return static_cast<int>((N + points_per_wg(ks, pb) - 1) / points_per_wg(ks, pb));
     };
 
-    // Too few wide point tiles to fill the GPU: first try narrow tiles (one
-    // point block per wave) if they fit in one round and K is at most 16
-    // centroid blocks; otherwise split K into enough ranges for one full
-    // round of workgroups, with at least two centroid blocks per K-range
-    // (every range pays the point prologue and the merge pass costs a
-    // launch, which a one-block range does not earn back).  Measured at
-    // N = 65536 (median us, settled, scratch kept per stream): D=64 K=16384:
-    // split 2 122.4, 3 127.7, 4 (one round) 113.3, 6 121.7, narrow 129.6;
-    // D=64 K=4096: narrow 36.0, split 3 39.1, 4 37.6; D=64 K=512: narrow
-    // 8.8, wide 13.9, split 12.6; D=128 K=4096: narrow 56.0, split 2 55.2,
-    // wide 89.4; D=128 K=512: narrow 11.4, wide 18.8, split 16.0; D=256
-    // K=4096: wide 104.5, narrow 103.9, split 2 112.7.  N=262144 D=128
-    // K=16384: wide direct 708.0, split 2 730.5.
+    // Too few wide point tiles to fill the GPU: either narrow tiles (one
+    // point block per wave; only while they fit in one round and K is at
+    // most 16 centroid blocks) or K split into ranges of wide tiles, as many
+    // as one round holds (rounded down: a second, nearly empty round costs
+    // a whole range's time) with at least two centroid blocks per range
+    // (every range pays the point prologue, and the merge pass a launch).
+    // The split is taken when it gives at least twice the narrow tiles'
+    // workgroups, i.e. when narrow tiles would leave half the CUs idle.
+    // Measured (median us, settled, scratch kept per stream; narrow / split
+    // s / direct wide):
+    //   N = 65536: D=64 K=4096 35.5 / s=4 39.6; D=64 K=2048 18.2 / s=4 24.5;
+    //     D=64 K=16384 126.9 / s=4 109.4; D=128 K=1024 18.5 / s=2 22.4;
+    //     D=128 K=2048 29.7 / 32.1; D=128 K=3072 42.2 / 43.2; D=128
+    //     K=4096 54.3 / 52.7; D=128 K=512 11.6 / 15.9.
+    //   smaller N: 49152 x 128 x 4096 49.0 / s=2 48.9 (s=3: 58.3);
+    //     40960 x 64 x 4096 27.9 / s=6 30.5; 32768 x 128 x 4096 48.9 /
+    //     s=4 33.8; 32768 x 64 x 4096 28.0 / s=8 26.0; 24576 x 128 x 4096
+    //     48.0 / s=5 32.8; 16384 x 128 x 4096 47.9 / s=8 25.1; 16384 x 32 x
+    //     4096 21.5 / s=8 18.7.
+    //   wide tiles only: 49152 x 128 x 16384 s=2 165.6 (s=3: 212.6, direct
+    //     285.6); 98304 x 128 x 4096 direct 82.3 (s=2, two rounds: 97.6).
     const int target_wgs = resident;
     int pb = wide;
-    if (force_path == 1 && force_count == 1)
+    int splits = 1;
+    const int wide_tiles = tiles_for(wide);
+    if (force_path == 1 && force_count == 1) {
         pb = 1;
-    else if (force_path == 0 && tiles_for(wide) < target_wgs && nkb <= 16 &&
-             tiles_for(1) <= resident)
-        pb = 1;
+    } else if (force_path == 0 && wide_tiles < target_wgs) {
+        int s = target_wgs / wide_tiles;
+        if (s > nkb / 2)
+            s = nkb / 2;
+        if (s < 1)
+            s = 1;
+        const bool narrow_ok = wide > 1 && nkb <= 16 && tiles_for(1) <= resident;
+        if (narrow_ok && static_cast<int64_t>(wide_tiles) * s < 2 * static_cast<int64_t>(tiles_for(1)))
+            pb = 1;
+        else
+            splits = s;
+    }
     pl.pb = pb;
     pl.ppw = points_per_wg(ks, pb);
     pl.tiles = tiles_for(pb);
     pl.wgs = pl.tiles;
 
-    int splits = 1;
     if (force_path == 2) {
         splits = force_count > 0 ? force_count : (target_wgs + pl.tiles - 1) / pl.tiles;
         if (splits < 1)
             splits = 1;
-    } else if (force_path == 0 && pb == wide && pl.tiles < target_wgs) {
-        splits = (target_wgs + pl.tiles - 1) / pl.tiles;
-        if (splits > nkb / 2)
-            splits = nkb / 2 > 1 ? nkb / 2 : 1;
     }
     const int need = min_k_ranges(D, K);   // C over 2 GiB: split regardless
     if (splits < need)

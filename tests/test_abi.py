@@ -173,6 +173,20 @@ def test_plan_for_the_sweep_shapes(lib):
         assert km.kmeans_plan(*shape) == p      # 0 CUs: the MI355X default
 
 
+@pytest.mark.parametrize("N,D,K,path,splits,wgs", [
+    (32768, 128, 4096, km.PATH_SPLIT, 4, 64),      # narrow tiles would fill half the CUs
+    (16384, 128, 4096, km.PATH_SPLIT, 8, 32),
+    (16384, 32, 4096, km.PATH_SPLIT, 8, 16),
+    (49152, 128, 16384, km.PATH_SPLIT, 2, 96),     # split count rounded down: one round
+    (98304, 128, 4096, km.PATH_DIRECT, 1, 192),    # not a two-round split
+    (40960, 64, 4096, km.PATH_DIRECT, 1, 160),     # narrow: the split has < 2x its workgroups
+    (49152, 128, 4096, km.PATH_DIRECT, 1, 192),
+])
+def test_plan_when_wide_tiles_underfill(lib, N, D, K, path, splits, wgs):
+    p = km.kmeans_plan(N, D, K, 256)
+    assert (p["path"], p["splits"], p["workgroups"]) == (path, splits, wgs), p
+
+
 def test_plan_follows_the_compute_unit_count(lib):
     assert km.kmeans_plan(65536, 128, 16384, 256)["splits"] == 2
     assert km.kmeans_plan(65536, 128, 16384, 128)["path"] == km.PATH_DIRECT

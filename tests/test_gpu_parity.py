@@ -350,6 +350,19 @@ def test_large_k_small_n():
 
 # ---------------------------------------------------------------- metamorphic
 
+@pytest.mark.parametrize("N,D,K", [(32768, 128, 4096), (16384, 32, 4096), (98304, 128, 1100),
+                                   (24576, 128, 4000)])
+def test_underfilled_shapes_take_their_plan_and_match(N, D, K):
+    """Shapes where wide tiles leave CUs idle: the automatic plan (a K split,
+    or direct wide tiles rather than a two-round split) against the oracle on
+    a sample, and bitwise against narrow tiles."""
+    X, C, _ = W.gaussian_mixture(N, D, K, 150 + D)
+    lab, md = run(X, C)
+    parity.check(X, C, lab, md, idx=parity.sample_indices(N, 151, 1024, 1024, 64))
+    ln, mn = run(X, C, km.PATH_DIRECT, 1)
+    assert np.array_equal(lab, ln) and md.tobytes() == mn.tobytes()
+
+
 @pytest.mark.parametrize("N,D,K", [(5000, 64, 4096), (20000, 128, 1000), (3000, 256, 777)])
 def test_split_equals_direct_bitwise(N, D, K):
     X, C, _ = W.gaussian_mixture(N, D, K, 90 + D)

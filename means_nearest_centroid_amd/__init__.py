@@ -16,6 +16,7 @@ CPU fallback: if the library is missing, the first call raises.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -104,22 +105,33 @@ def _check(lib, status: int):
 
 
 def _stream_handle(stream, device=None):
+    """The HIP stream to launch on, as an integer handle: ``stream``, or the
+    current stream of ``device`` (of the current device when None).  Calls
+    are often a few microseconds of GPU time, so this avoids building a
+    torch Stream object per call where torch exposes the raw handle."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    elif device is not None and stream.device != device:
+        index = device.index if device is not None else torch.cuda.current_device()
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(index)
+        return torch.cuda.current_stream(index).cuda_stream
+    if device is not None and stream.device != device:
         raise ValueError(f"stream is on {stream.device} but the tensors on {device}")
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
 
 
 def _on(device):
-    """The library launches on the current HIP device: make it the tensors'."""
+    """The library launches on the current HIP device: make it the tensors'
+    (a no-op context when it already is)."""
     import torch
+    if device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
     return torch.cuda.device(device)
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    return t.data_ptr() if t is not None else None
 
 
 def _matrix(t, name):

@@ -1773,8 +1773,10 @@ extern "C" kmeans_status_t kmeans_update_path(const void *X, const int32_t *labe
         return fail(KMEANS_ERR_ALIGNMENT, "labels, norms, counts and means must be 4-byte aligned");
 
     if (path == KMEANS_UPDATE_BUCKETS && !bucket_path_fits(N, K))
-        return fail(KMEANS_ERR_UNSUPPORTED, "the bucket path needs N <= 2^24 and K <= 4096 "
-                    "(N=%lld, K=%lld)", static_cast<long long>(N), static_cast<long long>(K));
+        return fail(KMEANS_ERR_UNSUPPORTED, "the bucket path needs N <= %lld and K <= %lld "
+                    "(N=%lld, K=%lld)", static_cast<long long>(kMaxBinPoints),
+                    static_cast<long long>(kMaxBinClusters), static_cast<long long>(N),
+                    static_cast<long long>(K));
     const UpdatePlan pl = make_update_plan(N, D, K, device_compute_units(), path);
     // The stream's scratch (none when N == 0), held until the launches are queued.
     std::unique_ptr<WorkspaceLease> lease;

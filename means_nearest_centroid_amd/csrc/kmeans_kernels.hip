@@ -645,6 +645,19 @@ __device__ KM_INLINE inline void assign_tile(
             }
         const bool improved = mn < bs[p];
         bs[p] = mn;                // mn <= bs[p]: the same value when not improved
+        // Wide D = 128 tile: the scheduler otherwise issues this block's
+        // dependent v_min3 chain as a burst after six of the next block's
+        // MFMAs; one VALU op after each MFMA measured 0.5-0.7% faster
+        // (with the priority split below) at 262144 x 128 x 4096, K = 16384
+        // and N = 1M.
+        if constexpr (G == 16 && KS == 8 && P > 1) {
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU op
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        }
         if (improved) {
             bt[p] = kt;
             if constexpr (DEFER) {
@@ -834,9 +847,19 @@ __device__ KM_INLINE inline void assign_tile(
             // runs alone.  Giving each wave of the pair the higher priority
             // for alternate pairs of tiles keeps them level (10% and 2% with
             // a switch every tile; every two tiles measured 0.3-0.5% faster
-            // than every tile or every four).
+            // than every tile or every four).  On the wide D = 128 tile the
+            // older wave leads on 3 of the 8 tiles (0, 1 and 4; bit j of
+            // kOlderLeads), which measured 0.1-0.3% faster again there and
+            // 2% slower on narrow tiles.
             if constexpr (kAlternatePriority) {
-                if (wave < WAVES / 2) {
+                if constexpr (KS == 8 && P > 1) {
+                    constexpr unsigned kOlderLeads = 0x13u;
+                    if (wave < WAVES / 2) {
+                        if ((kOlderLeads >> j) & 1u) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+                    } else {
+                        if ((kOlderLeads >> j) & 1u) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
+                    }
+                } else if (wave < WAVES / 2) {
                     if (j & 2) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
                 } else {
                     if (j & 2) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);

@@ -645,18 +645,20 @@ __device__ KM_INLINE inline void assign_tile(
             }
         const bool improved = mn < bs[p];
         bs[p] = mn;                // mn <= bs[p]: the same value when not improved
-        // Wide D = 128 tile: the scheduler otherwise issues this block's
-        // dependent v_min3 chain as a burst after six of the next block's
-        // MFMAs; one VALU op after each MFMA measured 0.5-0.7% faster
-        // (with the priority split below) at 262144 x 128 x 4096, K = 16384
-        // and N = 1M.
-        if constexpr (G == 16 && KS == 8 && P > 1) {
+        // 16x16x32 tiles at D = 128 and 256: the scheduler otherwise issues
+        // this block's dependent v_min3 chain as a burst after six of the
+        // next block's MFMAs; one VALU op after each of the first five
+        // MFMAs, then the block's other MFMAs (3 of 8 at D = 128, 11 of 16
+        // at D = 256), measured faster: wide D = 128 0.5-0.7% (with the
+        // priority split below), narrow D = 128 1.2-2.8%, D = 256 0.5-1.4%;
+        // at D = 64 (4 MFMAs per block) 1-2.5% slower, so not there.
+        if constexpr (G == 16 && KS >= 8) {
 #pragma unroll
             for (int i = 0; i < 5; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU op
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MB * NKS - 5, 0);
         }
         if (improved) {
             bt[p] = kt;

@@ -468,7 +468,9 @@ __device__ KM_INLINE inline void assign_tile(
     __shared__ __attribute__((aligned(16))) float n_st1[BK];
 
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // Wave-uniform, and said so: the LDS addresses of the DMAs below (M0)
+    // and the wave's branches are then scalar arithmetic.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pcol = lane % G;   // point column of a B block; row of an A block
     const int kq = lane / G;     // which 8-element group of a k-step
 
@@ -483,8 +485,7 @@ __device__ KM_INLINE inline void assign_tile(
     float xx[PB];
 
     // ---- centroid blocks: DMA into the LDS ring, norms via one register ----
-    const __amdgpu_buffer_rsrc_t cr = make_rsrc(C + static_cast<size_t>(k_begin) * D,
-                                                static_cast<uint32_t>(k_rows) * row_bytes);
+    const uint16_t *c_range = C + static_cast<size_t>(k_begin) * D;
     const __amdgpu_buffer_rsrc_t nr = make_rsrc(norms + k_begin, static_cast<uint32_t>(k_rows) * 4u);
     // Lane `lane` of DMA i writes LDS bytes [o, o+16) of the stage; fetch the
     // global chunk that the swizzled layout puts there (XOR is its own inverse).
@@ -495,12 +496,19 @@ __device__ KM_INLINE inline void assign_tile(
         const int r = o / ROW_BYTES, c = swz<S>(r, (o % ROW_BYTES) / 16);
         dma_src[i] = c * 8 < D ? static_cast<uint32_t>(r) * row_bytes + c * 16 : kOutOfRange;
     }
+    // One buffer resource per block (blk < the range's block count, so its
+    // size is positive), built with scalar arithmetic: each lane's offset
+    // is then dma_src as it stands, where an offset into one resource for
+    // the whole range cost an add, a compare and a select per DMA.  Rows
+    // past the range and the padding chunks stay out of range and land as
+    // zeros, as before.
     auto dma = [&](int blk, uint8_t *stage) KM_INLINE {
-        const uint32_t base = static_cast<uint32_t>(blk) * BK * row_bytes;
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(c_range + static_cast<size_t>(blk) * BK * D,
+                      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(k_rows - blk * BK) * row_bytes));
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i)
-            dma16(cr, (KM_LDS void *)(stage + (wave * DMA_PER_WAVE + i) * 1024),
-                  dma_src[i] == kOutOfRange ? kOutOfRange : dma_src[i] + base);
+            dma16(rb, (KM_LDS void *)(stage + (wave * DMA_PER_WAVE + i) * 1024), dma_src[i]);
     };
     uint32_t nbits = 0;
     bool nvalid = false;
